@@ -1,0 +1,330 @@
+"""CPU float64 oracle of the block-diffusion denoise step.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, links or calls
+this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may use it. It shares no code with the
+HIP library (no kernels, headers, helpers, tables or pre/post-processing);
+both sides only consume the same seeded input bytes.
+
+Every quantity is computed in numpy float64 from the plain definition of the
+step, without blocking, fusion or reordering beyond what the definition
+states. Sources (page title, section):
+
+* Attention of the active block -- Nemotron-TwoTower technical summary,
+  §Architecture (the denoiser uses bidirectional attention inside the noisy
+  block and causal cross-attention into the frozen context tower) and
+  §Generation (at every layer the denoiser attends to the context tower's KV
+  cache of past blocks and to the current block's bidirectional KV).
+* Exact prefix caching -- Hybrid Block Diffusion with Partial Bidirectionality
+  summary, technical §Method: the cached prefix state depends on the clean
+  prefix only, never on the diffusion step or on the active block.
+* Confidence unmasking (Algorithm 2) -- Nemotron-TwoTower technical summary,
+  §Training and conditioning, sampling bullet: all masked positions are
+  predicted in parallel, those whose confidence is above gamma are committed,
+  the others stay masked for further refinement.
+* Block loop (Algorithm 1) -- Nemotron-TwoTower technical summary,
+  §Generation: a block of S masked tokens is refined for T steps and then
+  committed.
+
+Readings where the pages are silent (all listed in the design doc):
+one softmax over prefix keys followed by block keys; every prefix key visible
+to every block query; no mask inside the block; scale tau = float32(1/sqrt(D))
+unless given; GQA head h reads KV head floor(h * Hkv / Hq); confidence = the
+maximum softmax probability at temperature 1; argmax ties -> lowest token
+index; commit iff p > gamma (strict) with gamma promoted from float32; when no
+masked position passes, the single most confident masked position commits
+(ties -> lowest position); at the last step every masked position commits;
+commits are final.
+
+Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
+things other than itself (library routines for special cases, closed forms,
+invariants, brute-force enumeration); see the docstrings below.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Iterable, Optional, Sequence
+
+import numpy as np
+
+NEAR_TIE_REL = 1e-4   # decisions closer than this (relative) are reported as near-ties
+
+
+# ----------------------------------------------------------------------------------------------
+# input decoding
+# ----------------------------------------------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly (bf16 is the top half of a float32)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def f32_to_f64(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def default_scale(D: int) -> float:
+    """Softmax scale tau: 1/sqrt(D) evaluated in float32, promoted exactly to float64."""
+    return float(np.float32(1.0) / np.sqrt(np.float32(D)))
+
+
+def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
+    """Contiguous GQA groups: query head h reads KV head floor(h * Hkv / Hq)."""
+    return (h * Hkv) // Hq
+
+
+# ----------------------------------------------------------------------------------------------
+# attention of the active block over [prefix ; block]
+# ----------------------------------------------------------------------------------------------
+def keys_values(k_blk, v_blk, k_cache, v_cache, prefix_len, b: int, g: int):
+    """Key/value rows visible to the block of sequence b through KV head g:
+    prefix rows 0..len_b-1 of the cache, then the S rows of the block (float64)."""
+    n = int(prefix_len[b])
+    K = np.concatenate([k_cache[b, g, :n, :], k_blk[b, :, g, :]], axis=0)
+    V = np.concatenate([v_cache[b, g, :n, :], v_blk[b, :, g, :]], axis=0)
+    return K, V
+
+
+def softmax_attention(Qr: np.ndarray, K: np.ndarray, V: np.ndarray, tau: float):
+    """O = softmax(tau * Qr K^T) V and LSE = ln sum exp(tau * Qr K^T), row-wise, float64."""
+    s = tau * (Qr @ K.T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    O = (e / z) @ V
+    lse = m[:, 0] + np.log(z[:, 0])
+    return O, lse
+
+
+def attn_step(q, k_blk, v_blk, k_cache, v_cache, prefix_len, scale: Optional[float] = None,
+              active: Optional[Sequence[int]] = None):
+    """One denoise-step attention for every (b, s, h).
+
+    q [B,S,Hq,D]; k_blk, v_blk [B,S,Hkv,D]; k_cache, v_cache [B,Hkv,Lcap,D];
+    prefix_len [B] -- all float64 (decode bf16 first). Returns O [B,S,Hq,D] and
+    LSE [B,Hq,S] (float64). Sequences with ``active[b] == 0`` get NaN rows
+    (the step does not touch them)."""
+    B, S, Hq, D = q.shape
+    Hkv = k_blk.shape[2]
+    tau = default_scale(D) if scale is None else float(np.float32(scale))
+    O = np.full((B, S, Hq, D), np.nan)
+    L = np.full((B, Hq, S), np.nan)
+    for b in range(B):
+        if active is not None and not active[b]:
+            continue
+        for h in range(Hq):
+            K, V = keys_values(k_blk, v_blk, k_cache, v_cache, prefix_len, b, kv_head_of(h, Hq, Hkv))
+            o, lse = softmax_attention(q[b, :, h, :], K, V, tau)
+            O[b, :, h, :] = o
+            L[b, h, :] = lse
+    return O, L
+
+
+def attn_rows(q, k_blk, v_blk, k_cache, v_cache, prefix_len, rows: Iterable, scale=None):
+    """Same definition for selected (b, s, h) triples only (full-size sampled checks).
+
+    Inputs may be bf16 bit arrays (uint16) or float64; only the slabs needed
+    are decoded. Returns {(b, s, h): (o[D], lse)}."""
+    dec = (lambda a: bf16_to_f64(a)) if np.asarray(q).dtype == np.uint16 else (lambda a: np.asarray(a, np.float64))
+    B, S, Hq, D = q.shape
+    Hkv = k_blk.shape[2]
+    tau = default_scale(D) if scale is None else float(np.float32(scale))
+    out = {}
+    by_bg = {}
+    for (b, s, h) in rows:
+        by_bg.setdefault((b, kv_head_of(h, Hq, Hkv)), []).append((b, s, h))
+    for (b, g), lst in by_bg.items():
+        n = int(prefix_len[b])
+        K = np.concatenate([dec(k_cache[b, g, :n, :]), dec(k_blk[b, :, g, :])], axis=0)
+        V = np.concatenate([dec(v_cache[b, g, :n, :]), dec(v_blk[b, :, g, :])], axis=0)
+        Qr = np.stack([dec(q[b, s, h, :]) for (_, s, h) in lst])
+        o, lse = softmax_attention(Qr, K, V, tau)
+        for i, key in enumerate(lst):
+            out[key] = (o[i], float(lse[i]))
+    return out
+
+
+def chunk_partials(Qr: np.ndarray, K: np.ndarray, V: np.ndarray, tau: float, bounds: Sequence[int]):
+    """Per key chunk [bounds[i], bounds[i+1]): running max m_c, l_c = sum exp(s - m_c) and
+    acc_c = sum exp(s - m_c) v. Empty chunks give m = -inf, l = 0, acc = 0."""
+    parts = []
+    s_all = tau * (Qr @ K.T)
+    for c0, c1 in zip(bounds[:-1], bounds[1:]):
+        if c1 <= c0:
+            parts.append((np.full(Qr.shape[0], -np.inf), np.zeros(Qr.shape[0]), np.zeros((Qr.shape[0], V.shape[1]))))
+            continue
+        s = s_all[:, c0:c1]
+        m = s.max(axis=1)
+        e = np.exp(s - m[:, None])
+        parts.append((m, e.sum(axis=1), e @ V[c0:c1]))
+    return parts
+
+
+def merge_partials(parts):
+    """Combine chunk partials: M = max_c m_c; O = sum_c acc_c e^(m_c - M) / sum_c l_c e^(m_c - M);
+    LSE = M + ln sum_c l_c e^(m_c - M). Chunks are combined in index order."""
+    M = np.max(np.stack([p[0] for p in parts]), axis=0)
+    num = np.zeros_like(parts[0][2])
+    den = np.zeros_like(parts[0][1])
+    for m, l, acc in parts:
+        w = np.where(np.isfinite(m), np.exp(m - M), 0.0)
+        num += acc * w[:, None]
+        den += l * w
+    return num / den[:, None], M + np.log(den)
+
+
+def attn_step_chunked(q, k_blk, v_blk, k_cache, v_cache, prefix_len, split_fn: Callable, scale=None):
+    """attn_step computed by splitting each (b, KV head) key sequence into chunks and merging.
+
+    ``split_fn(n_keys) -> bounds`` returns chunk boundaries 0 = c0 <= ... <= c_k = n_keys."""
+    B, S, Hq, D = q.shape
+    Hkv = k_blk.shape[2]
+    tau = default_scale(D) if scale is None else float(np.float32(scale))
+    O = np.zeros((B, S, Hq, D))
+    L = np.zeros((B, Hq, S))
+    for b in range(B):
+        for h in range(Hq):
+            K, V = keys_values(k_blk, v_blk, k_cache, v_cache, prefix_len, b, kv_head_of(h, Hq, Hkv))
+            bounds = list(split_fn(K.shape[0]))
+            assert bounds[0] == 0 and bounds[-1] == K.shape[0]
+            o, lse = merge_partials(chunk_partials(q[b, :, h, :], K, V, tau, bounds))
+            O[b, :, h, :] = o
+            L[b, h, :] = lse
+    return O, L
+
+
+# ----------------------------------------------------------------------------------------------
+# confidence unmasking
+# ----------------------------------------------------------------------------------------------
+def vocab_reduce(logits_row: np.ndarray):
+    """For one row l (float64): m = max_j l_j, a = min{j : l_j = m}, Z = sum_j exp(l_j - m),
+    p = 1 / Z (the maximum softmax probability)."""
+    m = float(np.max(logits_row))
+    a = int(np.flatnonzero(logits_row == m)[0])
+    Z = float(np.sum(np.exp(logits_row - m)))
+    return m, a, Z, 1.0 / Z
+
+
+def confidences(logits: np.ndarray, mask: np.ndarray, decode: Optional[Callable] = None):
+    """p and argmax for every masked row (unmasked rows: p = 0, argmax = -1).
+
+    ``logits`` is [rows, V] float32 or bf16 bits (uint16, with ``decode=bf16_to_f64``);
+    rows are decoded one at a time to keep memory bounded."""
+    rows = logits.shape[0]
+    p = np.zeros(rows)
+    a = np.full(rows, -1, dtype=np.int64)
+    for r in range(rows):
+        if mask[r]:
+            row = decode(logits[r]) if decode is not None else np.asarray(logits[r], np.float64)
+            _, a[r], _, p[r] = vocab_reduce(row)
+    return p, a
+
+
+def commit(p: np.ndarray, a: np.ndarray, mask: np.ndarray, tokens: np.ndarray, S: int,
+           gamma: float, min_commit: bool = True, commit_all: bool = False):
+    """Commit rule per sequence b (positions b*S .. b*S+S-1), in this order:
+    1. commit_all: C = every masked position;
+    2. else C = {s masked : p_s > gamma64}, gamma64 = float64(float32(gamma));
+    3. if C is empty, min_commit is set and some position is masked: C = {the masked s with
+       the largest p_s, ties -> lowest s}.
+    For s in C: tokens[s] = a_s, mask[s] = 0. Returns (mask, tokens, n_commit[B]) as new arrays."""
+    g64 = float(np.float32(gamma))
+    mask = np.array(mask, dtype=np.uint8, copy=True)
+    tokens = np.array(tokens, dtype=np.int32, copy=True)
+    B = mask.shape[0] // S
+    n_commit = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        idx = [b * S + s for s in range(S) if mask[b * S + s]]
+        if commit_all:
+            C = list(idx)
+        else:
+            C = [r for r in idx if p[r] > g64]
+            if not C and min_commit and idx:
+                best = idx[0]
+                for r in idx[1:]:
+                    if p[r] > p[best]:
+                        best = r
+                C = [best]
+        for r in C:
+            tokens[r] = a[r]
+            mask[r] = 0
+        n_commit[b] = len(C)
+    return mask, tokens, n_commit
+
+
+def confidence_unmask(logits, mask, tokens, S, gamma, min_commit=True, commit_all=False, decode=None):
+    """Vocabulary reduction of every masked row, then the commit rule.
+    Returns dict(mask, tokens, n_commit, conf, argmax)."""
+    p, a = confidences(logits, mask, decode)
+    m2, t2, n = commit(p, a, mask, tokens, S, gamma, min_commit, commit_all)
+    return {"mask": m2, "tokens": t2, "n_commit": n, "conf": p, "argmax": a}
+
+
+def margins(p: np.ndarray, mask: np.ndarray, S: int, gamma: float, min_commit=True, commit_all=False):
+    """Decision margins of the commit rule, to flag outcomes that float32 rounding could flip.
+
+    Returns a list of (kind, position or sequence, relative margin): 'gamma' for every masked row
+    (|p - gamma64| / gamma64) and 'fallback' for every sequence where the fallback fires (relative
+    gap between its two largest p; inf with a single masked position). Decisions with margin
+    < NEAR_TIE_REL are near-ties. Exactly equal p (bit-identical rows) are not near-ties: the
+    rule breaks them by position, deterministically on both sides."""
+    g64 = float(np.float32(gamma))
+    out = []
+    if commit_all:
+        return out
+    B = mask.shape[0] // S
+    for b in range(B):
+        idx = [b * S + s for s in range(S) if mask[b * S + s]]
+        for r in idx:
+            out.append(("gamma", r, abs(p[r] - g64) / g64 if g64 > 0 else math.inf))
+        if min_commit and idx and not any(p[r] > g64 for r in idx):
+            ps = sorted((p[r] for r in idx), reverse=True)
+            if len(ps) < 2 or ps[0] == ps[1]:
+                gap = math.inf
+            else:
+                gap = (ps[0] - ps[1]) / ps[0]
+            out.append(("fallback", b, gap))
+    return out
+
+
+def near_ties(p, mask, S, gamma, min_commit=True, commit_all=False, rel=NEAR_TIE_REL):
+    return [m for m in margins(p, mask, S, gamma, min_commit, commit_all) if m[2] < rel]
+
+
+# ----------------------------------------------------------------------------------------------
+# the T-step block loop
+# ----------------------------------------------------------------------------------------------
+def denoise_block(T: int, t0: int, B: int, S: int, mask0, tokens0, step_inputs: Callable,
+                  k_cache, v_cache, prefix_len, gamma: float, min_commit: bool = True,
+                  final_commit_all: bool = True, logits_decode=None, scale=None):
+    """Algorithm 1's inner loop for one block of every sequence.
+
+    For t = t0 .. T-1: a sequence is active iff it still has a masked position; if none is
+    active the loop stops. Active sequences get the attention of the step (q/k/v from
+    ``step_inputs(t)`` -> dict(q, k_blk, v_blk, logits), float64 q/k/v), then the confidence
+    unmasking of the step's logits with commit_all at t = T-1 (when ``final_commit_all``).
+    Returns dict(mask, tokens, steps_used[B], commits[T][B], and per executed step t: outs[t] (O),
+    conf[t], argmax[t], active[t], masks[t] (the mask at the start of step t))."""
+    mask = np.array(mask0, dtype=np.uint8, copy=True)
+    tokens = np.array(tokens0, dtype=np.int32, copy=True)
+    steps_used = np.zeros(B, dtype=np.int32)
+    commits = np.zeros((T, B), dtype=np.int32)
+    outs, confs, argmaxes, actives, masks = {}, {}, {}, {}, {}
+    for t in range(t0, T):
+        active = mask.reshape(B, S).any(axis=1)
+        if not active.any():
+            break
+        masks[t] = mask.copy()
+        inp = step_inputs(t)
+        O, _ = attn_step(inp["q"], inp["k_blk"], inp["v_blk"], k_cache, v_cache, prefix_len,
+                         scale=scale, active=active)
+        outs[t] = O
+        actives[t] = active.copy()
+        res = confidence_unmask(inp["logits"], mask, tokens, S, gamma, min_commit,
+                                commit_all=(final_commit_all and t == T - 1), decode=logits_decode)
+        confs[t], argmaxes[t] = res["conf"], res["argmax"]
+        mask, tokens = res["mask"], res["tokens"]
+        commits[t] = res["n_commit"]
+        steps_used[active] = t + 1
+    return {"mask": mask, "tokens": tokens, "steps_used": steps_used, "commits": commits,
+            "outs": outs, "conf": confs, "argmax": argmaxes, "active": actives, "masks": masks}
