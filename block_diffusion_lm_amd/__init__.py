@@ -1,0 +1,243 @@
+"""Block-diffusion denoise step on MI355X (gfx950): a thin Python binding over libbd.so.
+
+Every step of the path runs in the HIP kernels behind the C ABI (include/bd.h); this module only
+marshals torch tensors (device memory) and the current torch stream into those calls. There is
+no CPU or PyTorch fallback: a missing library raises.
+
+    attn_step(q, k_blk, v_blk, k_cache, v_cache, prefix_len, ...)  -> (out, lse)
+    confidence_unmask(logits, mask, tokens, block_len, gamma, ...)  -> dict
+    denoise_block(get_qkv, get_logits, k_cache, v_cache, prefix_len, mask, tokens, T, ...) -> dict
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Callable, Optional
+
+from . import _lib
+from ._lib import AttnDesc, BdError, StepHooks, UnmaskDesc  # noqa: F401
+
+__all__ = ["attn_step", "confidence_unmask", "denoise_block", "attn_desc", "unmask_desc", "Trace", "BdError",
+           "attn_workspace_bytes", "unmask_workspace_bytes", "denoise_workspace_bytes", "version"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev_tensor(t, name, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def version() -> str:
+    return _lib.load().bd_version().decode()
+
+
+def attn_desc(B, Hq, Hkv, D, S, prefix_capacity, max_prefix_len=None, softmax_scale=0.0, num_splits=0) -> AttnDesc:
+    return AttnDesc(B, Hq, Hkv, D, S, prefix_capacity,
+                    prefix_capacity if max_prefix_len is None else max_prefix_len, softmax_scale, num_splits)
+
+
+def unmask_desc(B, S, V, row_stride=None, bf16=True, gamma=0.9, min_commit=True, commit_all=False) -> UnmaskDesc:
+    return UnmaskDesc(B, S, V, V if row_stride is None else row_stride, _lib.BD_BF16 if bf16 else _lib.BD_F32,
+                      gamma, int(bool(min_commit)), int(bool(commit_all)))
+
+
+def attn_workspace_bytes(desc: AttnDesc) -> int:
+    return int(_lib.load().bd_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def unmask_workspace_bytes(desc: UnmaskDesc) -> int:
+    return int(_lib.load().bd_unmask_workspace_bytes(ctypes.byref(desc)))
+
+
+def denoise_workspace_bytes(ad: AttnDesc, ud: UnmaskDesc) -> int:
+    return int(_lib.load().bd_denoise_workspace_bytes(ctypes.byref(ad), ctypes.byref(ud)))
+
+
+def _workspace(nbytes, device, workspace):
+    torch = _torch()
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def attn_step(q, k_blk, v_blk, k_cache, v_cache, prefix_len, active=None, out=None, lse=None, want_lse=True,
+              max_prefix_len=None, softmax_scale=0.0, num_splits=0, workspace=None, stream=None):
+    """bd_attn_step on torch tensors. q [B,S,Hq,D], k_blk/v_blk [B,S,Hkv,D], k_cache/v_cache
+    [B,Hkv,Lcap,D] (bf16), prefix_len [B] int32, active [B] uint8 or None. Returns (out, lse)."""
+    torch = _torch()
+    L = _lib.load()
+    for t, n in ((q, "q"), (k_blk, "k_blk"), (v_blk, "v_blk"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev_tensor(t, n, torch.bfloat16)
+    _dev_tensor(prefix_len, "prefix_len", torch.int32)
+    if active is not None:
+        _dev_tensor(active, "active", torch.uint8)
+    B, S, Hq, D = q.shape
+    Hkv = k_blk.shape[2]
+    if k_blk.shape != (B, S, Hkv, D) or v_blk.shape != k_blk.shape:
+        raise ValueError("k_blk / v_blk must be [B, S, Hkv, D]")
+    if k_cache.shape[0] != B or k_cache.shape[1] != Hkv or k_cache.shape[3] != D or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache / v_cache must be [B, Hkv, Lcap, D]")
+    if prefix_len.shape != (B,):
+        raise ValueError("prefix_len must be [B]")
+    desc = attn_desc(B, Hq, Hkv, D, S, k_cache.shape[2], max_prefix_len, softmax_scale, num_splits)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    nbytes = L.bd_attn_workspace_bytes(ctypes.byref(desc))
+    ws = _workspace(nbytes, q.device, workspace)
+    _lib.check(L.bd_attn_step(ctypes.byref(desc), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(prefix_len), _ptr(active), _ptr(out), _ptr(lse), _ptr(ws),
+                              ws.numel() if ws is not None else 0, _stream(stream)), "bd_attn_step")
+    return out, lse
+
+
+def confidence_unmask(logits, mask, tokens, block_len, gamma, vocab=None, min_commit=True, commit_all=False,
+                      outputs=True, workspace=None, stream=None):
+    """bd_confidence_unmask on torch tensors. logits [B*S, row_stride] bf16 or float32; mask [B*S]
+    uint8 and tokens [B*S] int32 are updated in place. Returns dict(conf, argmax, n_commit)."""
+    torch = _torch()
+    L = _lib.load()
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("logits must be bfloat16 or float32")
+    _dev_tensor(logits, "logits")
+    _dev_tensor(mask, "mask", torch.uint8)
+    _dev_tensor(tokens, "tokens", torch.int32)
+    rows, stride = logits.shape
+    S = int(block_len)
+    if rows % S != 0 or mask.numel() != rows or tokens.numel() != rows:
+        raise ValueError("logits rows, mask and tokens must all be B*S")
+    B = rows // S
+    V = stride if vocab is None else vocab
+    desc = unmask_desc(B, S, V, stride, logits.dtype == torch.bfloat16, gamma, min_commit, commit_all)
+    conf = argmax = n_commit = None
+    if outputs:
+        conf = torch.empty(rows, dtype=torch.float32, device=logits.device)
+        argmax = torch.empty(rows, dtype=torch.int32, device=logits.device)
+        n_commit = torch.empty(B, dtype=torch.int32, device=logits.device)
+    nbytes = L.bd_unmask_workspace_bytes(ctypes.byref(desc))
+    ws = _workspace(nbytes, logits.device, workspace)
+    _lib.check(L.bd_confidence_unmask(ctypes.byref(desc), _ptr(logits), _ptr(mask), _ptr(tokens), _ptr(conf),
+                                      _ptr(argmax), _ptr(n_commit), _ptr(ws), ws.numel(), _stream(stream)),
+               "bd_confidence_unmask")
+    return {"conf": conf, "argmax": argmax, "n_commit": n_commit}
+
+
+def denoise_block(get_qkv: Callable, get_logits: Callable, k_cache, v_cache, prefix_len, mask, tokens, T: int,
+                  Hq: int, gamma: float, block_len: int, vocab: int, logits_bf16: bool = True, row_stride=None,
+                  t0: int = 0, min_commit=True, max_prefix_len=None, softmax_scale=0.0, num_splits=0, out=None,
+                  commits_per_step=True, workspace=None, stream=None):
+    """bd_denoise_block with Python hooks.
+
+    ``get_qkv(step, mask, tokens) -> (q, k_blk, v_blk)`` and ``get_logits(step, out) -> logits``
+    return device tensors (kept alive by this function until the next hook call). Returns
+    dict(out, steps_used, commits_per_step)."""
+    torch = _torch()
+    L = _lib.load()
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev_tensor(t, n, torch.bfloat16)
+    _dev_tensor(prefix_len, "prefix_len", torch.int32)
+    _dev_tensor(mask, "mask", torch.uint8)
+    _dev_tensor(tokens, "tokens", torch.int32)
+    B, Hkv, lcap, D = k_cache.shape
+    S = int(block_len)
+    ad = attn_desc(B, Hq, Hkv, D, S, lcap, max_prefix_len, softmax_scale, num_splits)
+    ud = unmask_desc(B, S, vocab, row_stride, logits_bf16, gamma, min_commit, False)
+    if out is None:
+        out = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=k_cache.device)
+    steps_used = torch.empty(B, dtype=torch.int32, device=k_cache.device)
+    cps = torch.zeros((T, B), dtype=torch.int32, device=k_cache.device) if commits_per_step else None
+    nbytes = L.bd_denoise_workspace_bytes(ctypes.byref(ad), ctypes.byref(ud))
+    ws = _workspace(nbytes, k_cache.device, workspace)
+    keep = {}
+    errors = []
+
+    def _qkv(user, step, mask_p, tokens_p, qp, kp, vp, stream_p):
+        try:
+            q, kb, vb = get_qkv(step, mask, tokens)
+            keep["qkv"] = (q, kb, vb)
+            qp[0], kp[0], vp[0] = q.data_ptr(), kb.data_ptr(), vb.data_ptr()
+            return _lib.BD_OK
+        except Exception as e:  # reported after the call returns
+            errors.append(e)
+            return _lib.BD_EINVAL
+
+    def _logits(user, step, out_p, lp, stream_p):
+        try:
+            lg = get_logits(step, out)
+            keep["logits"] = lg
+            lp[0] = lg.data_ptr()
+            return _lib.BD_OK
+        except Exception as e:
+            errors.append(e)
+            return _lib.BD_EINVAL
+
+    hooks = StepHooks(_lib.GET_QKV(_qkv), _lib.GET_LOGITS(_logits), None)
+    st = L.bd_denoise_block(ctypes.byref(ad), ctypes.byref(ud), T, t0, ctypes.byref(hooks), _ptr(k_cache),
+                            _ptr(v_cache), _ptr(prefix_len), _ptr(out), _ptr(mask), _ptr(tokens), _ptr(steps_used),
+                            _ptr(cps), _ptr(ws), ws.numel(), _stream(stream))
+    if errors:
+        raise errors[0]
+    _lib.check(st, "bd_denoise_block")
+    return {"out": out, "steps_used": steps_used, "commits_per_step": cps}
+
+
+class Trace:
+    """Kernel trace: while attached, every kernel libbd enqueues from this thread is bracketed by
+    HIP events on its stream. ``records()`` waits for them and returns [(kernel, ms)]."""
+
+    def __init__(self, capacity: int = 4096):
+        self._L = _lib.load()
+        h = ctypes.c_void_p()
+        _lib.check(self._L.bd_trace_create(capacity, ctypes.byref(h)), "bd_trace_create")
+        self.handle = h
+
+    def __enter__(self):
+        _lib.check(self._L.bd_trace_attach(self.handle), "bd_trace_attach")
+        return self
+
+    def __exit__(self, *exc):
+        self._L.bd_trace_attach(None)
+        return False
+
+    def clear(self):
+        _lib.check(self._L.bd_trace_clear(self.handle), "bd_trace_clear")
+
+    def records(self):
+        out = []
+        for i in range(self._L.bd_trace_count(self.handle)):
+            name = ctypes.c_char_p()
+            ms = ctypes.c_float()
+            _lib.check(self._L.bd_trace_get(self.handle, i, ctypes.byref(name), ctypes.byref(ms)), "bd_trace_get")
+            out.append((name.value.decode(), ms.value))
+        return out
+
+    def close(self):
+        if self.handle:
+            self._L.bd_trace_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,88 @@
+// Internal interface between the host side of the library (bd_api.cpp) and the HIP kernels
+// (bd_attn.hip, bd_unmask.hip). Not installed; the public ABI is include/bd.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bd {
+
+// ---------------------------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------------------------
+constexpr int kRowsPerWave = 64;   // two 32-row MFMA blocks per wave
+constexpr int kKeyTile = 64;       // keys staged through LDS per iteration
+
+struct AttnPlan {
+  int head_dim;       // D
+  int waves;          // waves per workgroup (1, 2 or 4); a workgroup owns waves*64 query rows
+  int rows;           // R = S * (Hq / Hkv): query rows per (sequence, KV head)
+  int row_tiles;      // ceil(R / (waves * 64))
+  int64_t chunk;      // keys per split (multiple of kKeyTile)
+  int nsplit;         // splits per (sequence, KV head)
+  int64_t n_items;    // B * Hkv * nsplit * row_tiles workgroups
+  bool direct;        // nsplit == 1: the split kernel writes the final output itself
+  size_t part_acc_off, part_ml_off, bytes;   // workspace layout
+};
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k_blk;
+  const uint16_t* v_blk;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* prefix_len;
+  const uint8_t* active;
+  uint16_t* out;
+  float* lse;
+  float* part_acc;    // [n_items][rows_pad][D]
+  float* part_ml;     // [n_items][rows_pad][2]: running max (log2 units) and sum
+  int B, S, Hq, Hkv, group, rows, rows_pad;
+  int64_t lcap;
+  int64_t chunk;
+  int nsplit, row_tiles;
+  float scale_log2;   // tau * log2(e)
+  int direct;
+};
+
+hipError_t launch_attn_split(const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_merge(const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------------
+// confidence unmasking
+// ---------------------------------------------------------------------------------------------
+struct UnmaskPlan {
+  int vsplit;          // vocabulary slices per row
+  int64_t slice;       // elements per slice (multiple of 8)
+  size_t bytes;
+};
+
+struct UnmaskArgs {
+  const void* logits;
+  int is_bf16;
+  int64_t row_stride;
+  int vocab;
+  int B, S;
+  uint8_t* mask;
+  int32_t* tokens;
+  float* conf;
+  int32_t* argmax;
+  int32_t* n_commit;
+  float gamma;
+  int min_commit, commit_all;
+  float* part;         // [B*S][vsplit][3]: max, index (as int bits), sum of exp
+  int vsplit;
+  int64_t slice;
+  // loop bookkeeping (all optional)
+  int step;
+  int32_t* steps_used;          // [B]: set to step+1 where the sequence had a masked position
+  uint8_t* active_next;         // [B]: whether a masked position remains after the commit
+};
+
+hipError_t launch_vocab_reduce(const UnmaskArgs& a, hipStream_t stream);
+hipError_t launch_commit(const UnmaskArgs& a, hipStream_t stream);
+hipError_t launch_loop_init(const uint8_t* mask, int B, int S, uint8_t* active, int32_t* steps_used,
+                            hipStream_t stream);
+
+}  // namespace bd

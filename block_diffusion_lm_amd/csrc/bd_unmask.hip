@@ -1,0 +1,230 @@
+// Confidence unmasking on gfx950.
+//
+// Source: Nemotron-TwoTower technical summary, §Training and conditioning, sampling bullet
+// (Algorithm 2): each step predicts every masked position in parallel; a position whose
+// confidence is above the threshold gamma is committed, the others stay masked; the number
+// committed per step therefore adapts. Confidence is the largest softmax probability of the
+// position's logits, p = 1 / sum_j exp(l_j - max_j l_j); the committed token is the lowest index
+// holding the maximum.
+//
+// vocab_reduce: one workgroup per (masked row, vocabulary slice) streams its slice once with
+// 16-byte loads and keeps, per thread, the running (max, first index of the max, sum of
+// exp(l - max)). The per-thread states are combined in a fixed order (wave butterflies, then the
+// four waves in index order), so a row always gives the same bits -- identical rows give
+// identical confidences. HBM-bound: every logit of a masked row is read exactly once.
+//
+// commit: one wave per sequence merges the slices of each of its S rows in slice order, then
+// applies the commit rule with ballots: threshold (strict >), or every masked position on the
+// last step, or -- when nothing passes -- the single most confident masked position (lowest
+// position on ties).
+#include "bd_internal.h"
+
+namespace bd {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Red {
+  float m;     // running max
+  int idx;     // first index holding m
+  float z;     // sum of exp(l - m)
+};
+
+// Combine two states; `a` covers lower indices than `b` whenever they hold equal maxima.
+__device__ __forceinline__ Red combine(Red a, Red b) {
+  Red r;
+  r.m = fmaxf(a.m, b.m);
+  if (r.m == -INFINITY) {
+    r.z = 0.f;
+    r.idx = min(a.idx, b.idx);
+    return r;
+  }
+  const float za = a.m == -INFINITY ? 0.f : a.z * __builtin_amdgcn_exp2f((a.m - r.m) * kLog2e);
+  const float zb = b.m == -INFINITY ? 0.f : b.z * __builtin_amdgcn_exp2f((b.m - r.m) * kLog2e);
+  r.z = za + zb;
+  r.idx = (a.m > b.m) ? a.idx : (b.m > a.m) ? b.idx : min(a.idx, b.idx);
+  return r;
+}
+
+__device__ __forceinline__ Red shfl_xor(Red a, int mask) {
+  Red r;
+  r.m = __shfl_xor(a.m, mask, 64);
+  r.idx = __shfl_xor(a.idx, mask, 64);
+  r.z = __shfl_xor(a.z, mask, 64);
+  return r;
+}
+
+// Fold n values (in index order, first index `base`) into the running state.
+template <int N>
+__device__ __forceinline__ void fold(Red& st, const float (&x)[N], int base) {
+  float lm = x[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) lm = fmaxf(lm, x[i]);
+  if (lm > st.m) {
+    int li = N - 1;
+#pragma unroll
+    for (int i = N - 1; i >= 0; --i)
+      if (x[i] == lm) li = i;
+    // rescale the old sum to the new max (old max -inf: nothing to keep)
+    st.z = (st.m == -INFINITY) ? 0.f : st.z * __builtin_amdgcn_exp2f((st.m - lm) * kLog2e);
+    st.m = lm;
+    st.idx = base + li;
+  }
+  if (st.m == -INFINITY) return;
+  const float mneg = -st.m * kLog2e;
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, mneg));
+  st.z += acc;
+}
+
+__device__ __forceinline__ float load_logit(const void* row, int is_bf16, int64_t j) {
+  if (is_bf16) return __uint_as_float((uint32_t)(reinterpret_cast<const uint16_t*>(row)[j]) << 16);
+  return reinterpret_cast<const float*>(row)[j];
+}
+
+__global__ __launch_bounds__(256) void vocab_reduce_kernel(UnmaskArgs a) {
+  const int64_t row = blockIdx.x / a.vsplit;
+  const int part = (int)(blockIdx.x % a.vsplit);
+  if (!a.mask[row]) return;
+  const int tid = threadIdx.x;
+  const int64_t v0 = (int64_t)part * a.slice;
+  const int64_t v1 = min(v0 + a.slice, (int64_t)a.vocab);
+  Red st{-INFINITY, 0x7fffffff, 0.f};
+  if (v0 < v1) {
+    const int elt = a.is_bf16 ? 2 : 4;
+    const char* rowp = reinterpret_cast<const char*>(a.logits) + row * a.row_stride * elt;
+    const int per = 16 / elt;                       // elements per 16-byte vector
+    const int64_t nvec = (v1 - v0) / per;           // full vectors of the slice
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + v0 * elt);
+    if (a.is_bf16) {
+      for (int64_t i = tid; i < nvec; i += 256) {
+        const u32x4 u = __builtin_nontemporal_load(vp + i);
+        float x[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          x[2 * w] = __uint_as_float(u[w] << 16);
+          x[2 * w + 1] = __uint_as_float(u[w] & 0xffff0000u);
+        }
+        fold<8>(st, x, (int)(v0 + i * 8));
+      }
+    } else {
+      for (int64_t i = tid; i < nvec; i += 256) {
+        const u32x4 u = __builtin_nontemporal_load(vp + i);
+        float x[4] = {__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]), __uint_as_float(u[3])};
+        fold<4>(st, x, (int)(v0 + i * 4));
+      }
+    }
+    // ragged tail of the slice (vocab not a multiple of the vector width)
+    for (int64_t j = v0 + nvec * per + tid; j < v1; j += 256) {
+      float x[1] = {load_logit(rowp, a.is_bf16, j)};
+      Red t{-INFINITY, 0x7fffffff, 0.f};
+      fold<1>(t, x, (int)j);
+      st = combine(st, t);
+    }
+  }
+  // Thread t saw vectors t, t+256, ...: for equal maxima the lower thread (or the tail, which
+  // comes after every full vector) holds the lower index, and combine() takes the minimum.
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) {
+    Red o = shfl_xor(st, msk);
+    // keep the operand order fixed for determinism: lower lane first
+    st = ((threadIdx.x & msk) == 0) ? combine(st, o) : combine(o, st);
+  }
+  __shared__ Red wred[4];
+  if ((tid & 63) == 0) wred[tid >> 6] = st;
+  __syncthreads();
+  if (tid == 0) {
+    Red r = wred[0];
+    for (int w = 1; w < 4; ++w) r = combine(r, wred[w]);
+    float* out = a.part + ((int64_t)row * a.vsplit + part) * 3;
+    out[0] = r.m;
+    out[1] = __int_as_float(r.idx);
+    out[2] = r.z;
+  }
+}
+
+__global__ __launch_bounds__(64) void commit_kernel(UnmaskArgs a) {
+  const int b = blockIdx.x;
+  const int s = threadIdx.x;
+  const bool in = s < a.S;
+  const int64_t r = (int64_t)b * a.S + s;
+  const bool masked = in && a.mask[r] != 0;
+  float p = 0.f;
+  int tok = -1;
+  if (masked) {
+    const float* pp = a.part + r * a.vsplit * 3;
+    Red st{pp[0], __float_as_int(pp[1]), pp[2]};
+    for (int c = 1; c < a.vsplit; ++c) st = combine(st, Red{pp[3 * c], __float_as_int(pp[3 * c + 1]), pp[3 * c + 2]});
+    p = 1.0f / st.z;
+    tok = st.idx;
+  }
+  if (in) {
+    if (a.conf) a.conf[r] = p;
+    if (a.argmax) a.argmax[r] = tok;
+  }
+  const uint64_t any_masked = __ballot(masked);
+  bool pass = masked && (a.commit_all || p > a.gamma);
+  uint64_t passed = __ballot(pass);
+  if (passed == 0 && a.min_commit && any_masked) {
+    // most confident masked position; lowest position on ties
+    float bp = masked ? p : -1.f;
+    int bs = masked ? s : 0x7fffffff;
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) {
+      const float op = __shfl_xor(bp, msk, 64);
+      const int os = __shfl_xor(bs, msk, 64);
+      if (op > bp || (op == bp && os < bs)) {
+        bp = op;
+        bs = os;
+      }
+    }
+    pass = masked && s == bs;
+    passed = __ballot(pass);
+  }
+  if (pass) {
+    a.tokens[r] = tok;
+    a.mask[r] = 0;
+  }
+  if (s == 0) {
+    if (a.n_commit) a.n_commit[b] = (int32_t)__popcll(passed);
+    if (a.steps_used && any_masked) a.steps_used[b] = a.step + 1;
+    if (a.active_next) a.active_next[b] = (any_masked & ~passed) != 0 ? 1 : 0;
+  }
+}
+
+__global__ __launch_bounds__(64) void loop_init_kernel(const uint8_t* mask, int S, uint8_t* active,
+                                                       int32_t* steps_used) {
+  const int b = blockIdx.x;
+  const int s = threadIdx.x;
+  const bool m = s < S && mask[(int64_t)b * S + s] != 0;
+  const uint64_t any = __ballot(m);
+  if (s == 0) {
+    active[b] = any != 0 ? 1 : 0;
+    steps_used[b] = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_vocab_reduce(const UnmaskArgs& a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.B * a.S * a.vsplit;
+  hipLaunchKernelGGL(vocab_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const UnmaskArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(commit_kernel, dim3((unsigned)a.B), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_loop_init(const uint8_t* mask, int B, int S, uint8_t* active, int32_t* steps_used,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(loop_init_kernel, dim3((unsigned)B), dim3(64), 0, stream, mask, S, active, steps_used);
+  return hipGetLastError();
+}
+
+}  // namespace bd

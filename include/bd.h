@@ -1,0 +1,207 @@
+/*
+ * bd.h -- C ABI of the block-diffusion denoise step for AMD MI355X (gfx950).
+ *
+ * One denoise step of a block-diffusion language model: the S positions of
+ * the active block attend bidirectionally to each other and to a read-only
+ * cache of the clean prefix's keys and values, then a confidence-unmasking
+ * pass commits the masked positions whose maximum softmax probability is
+ * above gamma. A T-step loop wraps the two.
+ *
+ * Sources (page title, section):
+ *  - Nemotron-TwoTower technical summary, §Architecture: the denoiser tower
+ *    uses bidirectional attention inside the noisy block and causal
+ *    cross-attention into the frozen context tower's layer-aligned KV cache.
+ *  - same page, §Generation (Algorithm 1): a block starts as S masked tokens
+ *    and is refined over T denoiser steps; at every layer the denoiser
+ *    attends to the context tower's KV cache of past blocks and to the
+ *    current block's bidirectional KV; the refined block is committed.
+ *  - same page, §Training and conditioning, sampling bullet (Algorithm 2):
+ *    every step predicts all masked positions in parallel and commits those
+ *    whose confidence exceeds gamma; the rest stay masked.
+ *  - Hybrid Block Diffusion with Partial Bidirectionality summary, technical
+ *    §Method: the prefix cache is a function of the clean prefix only, so the
+ *    step never writes it.
+ *
+ * Conventions (every entry point):
+ *  - Pointers are DEVICE pointers unless marked (host). The caller owns every
+ *    buffer; the library never allocates or frees device memory on these
+ *    paths and keeps no pointer after returning.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *    is the null stream). Results are valid once the stream is synchronised.
+ *    No entry point synchronises the stream.
+ *  - Arguments are validated on the host before anything is enqueued. On a
+ *    non-OK status nothing has been enqueued (BD_EHIP: a launch failed) and
+ *    bd_last_error() describes the cause.
+ *  - Alignment: every tensor base pointer must be 16-byte aligned; row
+ *    strides must be multiples of 16 bytes.
+ *  - Inputs must be finite, except logits, which may hold -inf (each
+ *    evaluated row must hold at least one finite value).
+ *  - Calls that share a workspace, or overlapping output buffers, must not
+ *    run concurrently.
+ */
+#ifndef BD_H
+#define BD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BD_OK = 0,
+  BD_EINVAL = 1,        /* invalid argument (null pointer, shape, range, alignment) */
+  BD_EUNSUPPORTED = 2,  /* valid but not supported by this build (e.g. head_dim 96) */
+  BD_EWORKSPACE = 3,    /* workspace smaller than the *_workspace_bytes query */
+  BD_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+} bd_status;
+
+typedef enum { BD_BF16 = 0, BD_F32 = 1 } bd_dtype;
+
+/* ------------------------------------------------------------------------------------------
+ * Attention of the active block over [prefix ; block]
+ *
+ * For sequence b, block position s and query head h (GQA: KV head
+ * g = floor(h * Hkv / Hq), contiguous groups), with keys/values
+ *   K_b,g = [ k_cache[b, g, 0 .. prefix_len[b]-1, :] ; k_blk[b, 0 .. S-1, g, :] ]
+ * (likewise V) and tau = softmax_scale:
+ *   out[b, s, h, :] = softmax_j(tau * q[b,s,h,:] . K_b,g[j,:]) V_b,g
+ *   lse[b, h, s]    = ln sum_j exp(tau * q[b,s,h,:] . K_b,g[j,:])
+ * One softmax runs over every prefix key and every block key; there is no
+ * mask inside the block (every block position sees every other) and every
+ * prefix key is visible to every block query. Positions are not applied here
+ * (rotary embeddings, if any, are already in q and k).
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;            /* B >= 1 */
+  int32_t n_q_heads;        /* Hq >= 1, Hq % Hkv == 0 */
+  int32_t n_kv_heads;       /* Hkv >= 1 */
+  int32_t head_dim;         /* D: 64 or 128 */
+  int32_t block_len;        /* S: 1 .. 64 */
+  int64_t prefix_capacity;  /* Lcap >= 1: token stride of k_cache / v_cache */
+  int64_t max_prefix_len;   /* host upper bound on every prefix_len[b]; 0 .. Lcap; used to plan the split */
+  float softmax_scale;      /* tau; <= 0 selects 1/sqrt(D) computed in float32 */
+  int32_t num_splits;       /* 0 = automatic; > 0 forces the number of key chunks per (b, KV head) */
+} bd_attn_desc;
+
+/* Workspace bytes bd_attn_step needs for this descriptor (0 on an invalid descriptor). */
+size_t bd_attn_workspace_bytes(const bd_attn_desc* desc);
+
+/* q:        bf16 [B, S, Hq, D]            (read only)
+ * k_blk:    bf16 [B, S, Hkv, D]           (read only)  keys of the active block
+ * v_blk:    bf16 [B, S, Hkv, D]           (read only)
+ * k_cache:  bf16 [B, Hkv, Lcap, D]        (read only)  prefix keys; rows >= prefix_len[b] are never read
+ * v_cache:  bf16 [B, Hkv, Lcap, D]        (read only)
+ * prefix_len: int32 [B], 0 <= prefix_len[b] <= max_prefix_len (device-side precondition)
+ * active:   uint8 [B] or NULL (all active). Sequences with active[b] == 0 are skipped: their rows
+ *           of out and lse are left untouched.
+ * out:      bf16 [B, S, Hq, D]  (written; rounded to nearest even)
+ * lse:      float32 [B, Hq, S] or NULL
+ * workspace: device scratch of at least bd_attn_workspace_bytes(desc) bytes. */
+bd_status bd_attn_step(const bd_attn_desc* desc,
+                       const void* q, const void* k_blk, const void* v_blk,
+                       const void* k_cache, const void* v_cache,
+                       const int32_t* prefix_len, const uint8_t* active,
+                       void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Confidence unmasking
+ *
+ * For every masked row r (mask[r] == 1) of the logits:
+ *   m_r = max_j l_rj,  a_r = min{ j : l_rj = m_r } (lowest index wins ties),
+ *   p_r = 1 / sum_j exp(l_rj - m_r)   (the maximum softmax probability).
+ * Rows with mask[r] == 0 are not read. Then, per sequence b (rows b*S .. b*S+S-1):
+ *   C = every masked position                        if commit_all,
+ *   C = { masked s : p_s > gamma }  (strict, float32)  otherwise;
+ *   if C is empty, min_commit is set and a position is masked, C = { the masked position with
+ *   the largest p, lowest position on ties };
+ *   for s in C: tokens[s] = a_s, mask[s] = 0.  Commits are final.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;         /* B >= 1 */
+  int32_t block_len;     /* S: 1 .. 64 */
+  int32_t vocab;         /* V >= 1 */
+  int64_t row_stride;    /* elements between consecutive logit rows, >= V */
+  bd_dtype logits_dtype; /* BD_BF16 or BD_F32 */
+  float gamma;           /* threshold in [0, 1]; commit iff p > gamma */
+  int32_t min_commit;    /* 1: commit the most confident masked position when none passes */
+  int32_t commit_all;    /* 1: commit every masked position (last step of a block) */
+} bd_unmask_desc;
+
+size_t bd_unmask_workspace_bytes(const bd_unmask_desc* desc);
+
+/* logits:   [B*S, row_stride] of logits_dtype (read only)
+ * mask:     uint8 [B*S], 1 = masked (read, then updated in place)
+ * tokens:   int32 [B*S] (committed positions are written)
+ * conf:     float32 [B*S] or NULL: p_r of masked rows, 0 for rows that were not masked
+ * argmax:   int32 [B*S] or NULL: a_r of masked rows, -1 for rows that were not masked
+ * n_commit: int32 [B] or NULL: |C| per sequence */
+bd_status bd_confidence_unmask(const bd_unmask_desc* desc, const void* logits,
+                               uint8_t* mask, int32_t* tokens,
+                               float* conf, int32_t* argmax, int32_t* n_commit,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * The T-step block loop (Algorithm 1's inner loop)
+ *
+ * For t = t0 .. T-1: sequences with a masked position are active; the model hooks provide the
+ * step's q / k_blk / v_blk, bd_attn_step runs for the active sequences into `out`, the hooks
+ * turn `out` into logits, and bd_confidence_unmask runs with commit_all = (t == T-1). Sequences
+ * without a masked position skip all work on the device; there is no host synchronisation
+ * inside the loop (every step is enqueued, inactive work exits at once).
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+  /* Return device pointers (valid until the next hook call) to the step's q [B,S,Hq,D],
+   * k_blk and v_blk [B,S,Hkv,D] (bf16). May enqueue work on `stream`. Non-OK aborts the loop. */
+  bd_status (*get_qkv)(void* user, int32_t step, const uint8_t* mask, const int32_t* tokens,
+                       const void** q, const void** k_blk, const void** v_blk, void* stream);
+  /* Return a device pointer to the step's logits [B*S, row_stride] computed from attn_out. */
+  bd_status (*get_logits)(void* user, int32_t step, const void* attn_out, const void** logits,
+                          void* stream);
+  void* user;
+} bd_step_hooks;
+
+size_t bd_denoise_workspace_bytes(const bd_attn_desc* attn, const bd_unmask_desc* unmask);
+
+/* attn / unmask: descriptors as above (unmask->commit_all is ignored; the loop sets it).
+ * T >= 1 steps, 0 <= t0 < T (resume from step t0 with the caller's mask and tokens).
+ * out:        bf16 [B,S,Hq,D], rewritten every step for the active sequences.
+ * mask/tokens: as in bd_confidence_unmask, updated step by step.
+ * steps_used: int32 [B] (required): t+1 of the last step at which b was active, 0 if never.
+ * commits_per_step: int32 [T, B] or NULL: rows t0 .. T-1 receive n_commit of each step. */
+bd_status bd_denoise_block(const bd_attn_desc* attn, const bd_unmask_desc* unmask,
+                           int32_t T, int32_t t0, const bd_step_hooks* hooks,
+                           const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+                           void* out, uint8_t* mask, int32_t* tokens,
+                           int32_t* steps_used, int32_t* commits_per_step,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Thread-local message describing this thread's last non-OK status ("" if none). */
+const char* bd_last_error(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Kernel tracing (observability; off unless a trace is attached)
+ *
+ * While a trace is attached to the calling thread, every kernel the library enqueues from that
+ * thread is bracketed by two HIP events recorded on the launch stream. bd_trace_get waits for
+ * the events of record i and returns the kernel name and its duration.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct bd_trace bd_trace;
+
+bd_status bd_trace_create(int32_t capacity, bd_trace** out);   /* capacity: records kept */
+void bd_trace_destroy(bd_trace* trace);
+bd_status bd_trace_attach(bd_trace* trace);                     /* NULL detaches */
+bd_status bd_trace_clear(bd_trace* trace);
+int32_t bd_trace_count(const bd_trace* trace);                  /* records taken (<= capacity) */
+bd_status bd_trace_get(const bd_trace* trace, int32_t i, const char** kernel, float* ms);
+
+/* Library version string, e.g. "bd 0.1.0 gfx950". */
+const char* bd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BD_H */

@@ -1,0 +1,60 @@
+"""Helpers shared by the GPU parity tests (device transfer, tolerances, guard canaries)."""
+import numpy as np
+import torch
+
+ATOL = 2e-2      # attention: max-abs bound (bf16 in, fp32 accumulate)
+RTOL_L2 = 1e-2   # attention: relative L2 bound
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> contiguous bf16 device tensor (same bytes)."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def bf16_f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_attn_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert err.max() <= ATOL, f"{what}: max-abs {err.max():.3e} > {ATOL}"
+    assert rel <= RTOL_L2, f"{what}: rel-L2 {rel:.3e} > {RTOL_L2}"
+    return err.max(), rel
+
+
+def guarded(shape, dtype, guard=64, fill=None):
+    """A device tensor view with canary regions before and after it (all inside one allocation)."""
+    n = int(np.prod(shape))
+    big = torch.empty(n + 2 * guard, dtype=dtype, device="cuda")
+    if dtype == torch.bfloat16:
+        big.view(torch.int16).fill_(0x7F81)   # a NaN pattern
+    elif dtype == torch.float32:
+        big.fill_(float("nan"))
+    else:
+        big.fill_(-77 if dtype != torch.uint8 else 0xA5)
+    view = big[guard:guard + n].view(shape)
+    if fill is not None:
+        view.copy_(fill)
+    return big, view, guard
+
+
+def guards_intact(big: torch.Tensor, guard: int, n: int, ref_big_before: torch.Tensor) -> bool:
+    a = big.view(torch.uint8) if big.dtype != torch.uint8 else big
+    b = ref_big_before.view(torch.uint8) if ref_big_before.dtype != torch.uint8 else ref_big_before
+    esz = big.element_size()
+    lo = slice(0, guard * esz)
+    hi = slice((guard + n) * esz, None)
+    return bool(torch.equal(a[lo], b[lo]) and torch.equal(a[hi], b[hi]))

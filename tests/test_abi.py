@@ -1,0 +1,167 @@
+"""CPU tier of the C ABI: the library loads, exports every entry point include/bd.h declares, and
+rejects invalid arguments on the host before anything is enqueued (no GPU needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from block_diffusion_lm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "bd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = set()
+    for m in re.finditer(r"^[A-Za-z_][\w \t\*]*?\b(bd_\w+)\s*\(", src, flags=re.M):
+        if "(*" in m.group(0):
+            continue
+        names.add(m.group(1))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_diffusion_lm_amd.build import build
+        build()
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 14, names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in bd.h but not exported"
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_version(L):
+    assert b"gfx950" in L.bd_version()
+
+
+def good_attn():
+    return _lib.AttnDesc(2, 32, 2, 128, 16, 4096, 4096, 0.0, 0)
+
+
+def call_attn(L, d, ptr=16 * 1024, ws=None, nbytes=None):
+    if nbytes is None:
+        nbytes = L.bd_attn_workspace_bytes(ctypes.byref(d))
+    p = ctypes.c_void_p(ptr)
+    return L.bd_attn_step(ctypes.byref(d), p, p, p, p, p, p, None, p, None, ws if ws is not None else p, nbytes, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, _lib.BD_EINVAL),
+    ("n_kv_heads", 3, _lib.BD_EINVAL),          # 32 % 3 != 0
+    ("head_dim", 96, _lib.BD_EUNSUPPORTED),
+    ("block_len", 0, _lib.BD_EINVAL),
+    ("block_len", 65, _lib.BD_EINVAL),
+    ("max_prefix_len", 5000, _lib.BD_EINVAL),   # > capacity
+    ("prefix_capacity", 0, _lib.BD_EINVAL),
+    ("num_splits", -1, _lib.BD_EINVAL),
+    ("softmax_scale", math.nan, _lib.BD_EINVAL),
+])
+def test_attn_descriptor_validation(L, field, value, status):
+    d = good_attn()
+    setattr(d, field, value)
+    assert L.bd_attn_workspace_bytes(ctypes.byref(d)) == 0
+    assert call_attn(L, d) == status
+    assert L.bd_last_error()
+
+
+def test_attn_pointer_validation(L):
+    d = good_attn()
+    nb = L.bd_attn_workspace_bytes(ctypes.byref(d))
+    assert nb > 0     # this shape is split: partials need a workspace
+    p = ctypes.c_void_p(4096)
+    bad = ctypes.c_void_p(4096 + 2)
+    args = [p] * 6
+    for i in range(6):
+        a = list(args)
+        a[i] = None
+        assert L.bd_attn_step(ctypes.byref(d), *a, None, p, None, p, nb, None) == _lib.BD_EINVAL
+        a[i] = bad
+        assert L.bd_attn_step(ctypes.byref(d), *a, None, p, None, p, nb, None) == _lib.BD_EINVAL
+    # output NULL
+    assert L.bd_attn_step(ctypes.byref(d), *args, None, None, None, p, nb, None) == _lib.BD_EINVAL
+    # workspace too small / misaligned
+    assert call_attn(L, d, nbytes=nb - 1) == _lib.BD_EWORKSPACE
+    assert b"workspace too small" in L.bd_last_error()
+    assert call_attn(L, d, ws=ctypes.c_void_p(4096 + 16), nbytes=nb) == _lib.BD_EINVAL
+
+
+def test_small_problem_needs_no_workspace(L):
+    d = _lib.AttnDesc(1, 8, 2, 64, 16, 256, 256, 0.0, 0)
+    assert L.bd_attn_workspace_bytes(ctypes.byref(d)) == 0
+    d.num_splits = 3
+    assert L.bd_attn_workspace_bytes(ctypes.byref(d)) > 0
+
+
+def good_unmask():
+    return _lib.UnmaskDesc(2, 16, 131072, 131072, _lib.BD_BF16, 0.9, 1, 0)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("batch", 0), ("block_len", 65), ("vocab", 0), ("row_stride", 100), ("logits_dtype", 7),
+    ("gamma", math.nan), ("gamma", -0.1), ("gamma", 1.5), ("min_commit", 2), ("commit_all", -1),
+])
+def test_unmask_descriptor_validation(L, field, value):
+    d = good_unmask()
+    setattr(d, field, value)
+    p = ctypes.c_void_p(4096)
+    assert L.bd_unmask_workspace_bytes(ctypes.byref(d)) == 0
+    assert L.bd_confidence_unmask(ctypes.byref(d), p, p, p, None, None, None, p, 1 << 20, None) == _lib.BD_EINVAL
+
+
+def test_unmask_stride_alignment(L):
+    d = _lib.UnmaskDesc(1, 16, 1001, 1001, _lib.BD_BF16, 0.9, 1, 0)   # 2002-byte rows
+    p = ctypes.c_void_p(4096)
+    assert L.bd_confidence_unmask(ctypes.byref(d), p, p, p, None, None, None, p, 1 << 20, None) == _lib.BD_EINVAL
+    d.row_stride = 1008
+    assert L.bd_unmask_workspace_bytes(ctypes.byref(d)) > 0
+
+
+def test_unmask_pointer_validation(L):
+    d = good_unmask()
+    nb = L.bd_unmask_workspace_bytes(ctypes.byref(d))
+    p = ctypes.c_void_p(4096)
+    assert L.bd_confidence_unmask(ctypes.byref(d), None, p, p, None, None, None, p, nb, None) == _lib.BD_EINVAL
+    assert L.bd_confidence_unmask(ctypes.byref(d), ctypes.c_void_p(4100), p, p, None, None, None, p, nb, None) == _lib.BD_EINVAL
+    assert L.bd_confidence_unmask(ctypes.byref(d), p, None, p, None, None, None, p, nb, None) == _lib.BD_EINVAL
+    assert L.bd_confidence_unmask(ctypes.byref(d), p, p, None, None, None, None, p, nb, None) == _lib.BD_EINVAL
+    assert L.bd_confidence_unmask(ctypes.byref(d), p, p, p, None, None, None, p, nb - 1, None) == _lib.BD_EWORKSPACE
+
+
+def test_denoise_validation(L):
+    ad = good_attn()
+    ud = good_unmask()
+    nb = L.bd_denoise_workspace_bytes(ctypes.byref(ad), ctypes.byref(ud))
+    assert nb >= L.bd_attn_workspace_bytes(ctypes.byref(ad)) + L.bd_unmask_workspace_bytes(ctypes.byref(ud))
+    p = ctypes.c_void_p(4096)
+    hooks = _lib.StepHooks(_lib.GET_QKV(lambda *a: 0), _lib.GET_LOGITS(lambda *a: 0), None)
+
+    def run(T=8, t0=0, h=hooks, ws_bytes=nb, ad_=ad, ud_=ud, steps=p):
+        return L.bd_denoise_block(ctypes.byref(ad_), ctypes.byref(ud_), T, t0, ctypes.byref(h) if h else None, p, p, p,
+                                  p, p, p, steps, None, p, ws_bytes, None)
+
+    assert run(T=0) == _lib.BD_EINVAL
+    assert run(t0=8) == _lib.BD_EINVAL
+    assert run(t0=-1) == _lib.BD_EINVAL
+    assert run(h=None) == _lib.BD_EINVAL
+    assert run(steps=None) == _lib.BD_EINVAL
+    assert run(ws_bytes=nb - 1) == _lib.BD_EWORKSPACE
+    ud2 = good_unmask()
+    ud2.block_len = 32
+    assert run(ud_=ud2) == _lib.BD_EINVAL
+    assert L.bd_denoise_workspace_bytes(ctypes.byref(ad), ctypes.byref(ud2)) == 0
+
+
+def test_trace_lifecycle_without_gpu(L):
+    h = ctypes.c_void_p()
+    assert L.bd_trace_create(0, ctypes.byref(h)) == _lib.BD_EINVAL
+    assert L.bd_trace_count(None) == 0
+    assert L.bd_trace_get(None, 0, None, None) == _lib.BD_EINVAL

@@ -1,0 +1,150 @@
+"""GPU parity of bd_attn_step against the float64 oracle (through the C ABI).
+
+Small shapes (whole tensors compared) span several key tiles, several splits, ragged tails,
+padded row tiles, S = 1 (AR decode), L = 0 and head_dim 64/128. The official workloads run at
+full size in the launch configuration the benchmark uses, checked on sampled rows the oracle
+computes one by one, plus properties that hold at any size (determinism, the cache is never
+written, inactive sequences untouched, canaries around the output intact)."""
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_lm_amd as bd
+from block_diffusion_lm_amd import inputs as I
+from oracle import bd_oracle as O
+from tests.gpu_util import assert_attn_close, bf16_f64, dev, dev_bf16, guarded, guards_intact, host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(inp, **kw):
+    t = {k: dev_bf16(inp[k]) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
+    t["prefix_len"] = dev(inp["prefix_len"])
+    out, lse = bd.attn_step(t["q"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], t["prefix_len"], **kw)
+    torch.cuda.synchronize()
+    return host_f64(out), lse.cpu().numpy().astype(np.float64), t
+
+
+def oracle_full(inp, active=None):
+    f = {k: bf16_f64(inp[k]) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
+    return O.attn_step(f["q"], f["k_blk"], f["v_blk"], f["k_cache"], f["v_cache"], inp["prefix_len"], active=active)
+
+
+SMALL = [
+    # name, B, Hq, Hkv, D, S, prefix_len
+    ("tiny-like", 1, 8, 2, 64, 16, 256),
+    ("ragged-d128", 3, 32, 2, 128, 16, (1, 700)),
+    ("no-prefix", 2, 8, 2, 64, 16, 0),
+    ("ar-decode-S1", 2, 32, 8, 128, 1, (60, 300)),
+    ("S32-two-row-tiles", 1, 32, 2, 128, 32, 333),
+    ("padded-rows", 2, 6, 3, 64, 5, (0, 129)),
+    ("S64-g4", 1, 16, 4, 128, 64, 190),
+    ("mha-D64", 2, 4, 4, 64, 16, 77),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 7])
+def test_small_shapes_match_oracle(case, num_splits):
+    name, B, Hq, Hkv, D, S, L = case
+    w = I.small_workload(name, B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, prefix_len=L, wid=200 + SMALL.index(case))
+    inp = I.attn_inputs(w)
+    print(f"[attn] {name} splits={num_splits} lens={inp['prefix_len'].tolist()}", flush=True)
+    got, lse, _ = run_gpu(inp, num_splits=num_splits)
+    ref, ref_lse = oracle_full(inp)
+    assert_attn_close(got, ref, name)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-4, atol=1e-3)
+
+
+def test_tiny_workload_and_planted_large_scores():
+    w = I.WORKLOADS["tiny"]
+    inp = I.attn_inputs(w)
+    got, lse, _ = run_gpu(inp)
+    ref, ref_lse = oracle_full(inp)
+    assert_attn_close(got, ref, "tiny")
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-4, atol=1e-3)
+    # planted large scores: one prefix key per KV head aligned with every query -> O ~ its V row (O(1))
+    inp2 = {k: v.copy() for k, v in inp.items()}
+    qf = bf16_f64(inp2["q"])
+    kc = bf16_f64(inp2["k_cache"])
+    kc[:, :, 17, :] = 0.0
+    kc[:, :, 17, 0] = 8.0
+    qf[..., 0] = 16.0
+    inp2["q"] = I.f32_to_bf16_bits(qf.astype(np.float32))
+    inp2["k_cache"] = I.f32_to_bf16_bits(kc.astype(np.float32))
+    got2, _, _ = run_gpu(inp2)
+    ref2, _ = oracle_full(inp2)
+    assert np.abs(ref2).max() > 0.5
+    assert_attn_close(got2, ref2, "planted")
+
+
+def test_block_permutation_on_gpu():
+    w = I.small_workload("perm", B=2, Hq=32, Hkv=2, D=128, S=16, prefix_len=(100, 500), wid=230)
+    inp = I.attn_inputs(w)
+    perm = np.random.default_rng(0).permutation(16)
+    inp2 = dict(inp)
+    for k in ("q", "k_blk", "v_blk"):
+        inp2[k] = np.ascontiguousarray(inp[k][:, perm])
+    a, _, _ = run_gpu(inp)
+    b, _, _ = run_gpu(inp2)
+    np.testing.assert_allclose(b, a[:, perm], atol=4e-3)
+
+
+def test_determinism_and_cache_untouched():
+    w = I.small_workload("det", B=2, Hq=32, Hkv=2, D=128, S=16, prefix_len=(3000, 5000), wid=231)
+    inp = I.attn_inputs(w)
+    t = {k: dev_bf16(inp[k]) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
+    t["prefix_len"] = dev(inp["prefix_len"])
+    before = {k: v.clone() for k, v in t.items()}
+    o1, l1 = bd.attn_step(t["q"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], t["prefix_len"])
+    o2, l2 = bd.attn_step(t["q"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], t["prefix_len"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    for k in t:
+        assert torch.equal(t[k].view(torch.uint8) if t[k].dtype != torch.int32 else t[k],
+                           before[k].view(torch.uint8) if before[k].dtype != torch.int32 else before[k]), k
+
+
+def test_inactive_sequences_and_canaries():
+    w = I.small_workload("act", B=3, Hq=8, Hkv=2, D=64, S=16, prefix_len=(10, 900), wid=232)
+    inp = I.attn_inputs(w)
+    t = {k: dev_bf16(inp[k]) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
+    t["prefix_len"] = dev(inp["prefix_len"])
+    active = torch.tensor([1, 0, 1], dtype=torch.uint8, device="cuda")
+    for splits in (0, 3):
+        big, out, g = guarded(tuple(inp["q"].shape), torch.bfloat16)
+        lbig, lse, lg = guarded((3, 8, 16), torch.float32)
+        b0, l0 = big.clone(), lbig.clone()
+        bd.attn_step(t["q"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], t["prefix_len"], active=active,
+                     out=out, lse=lse, num_splits=splits)
+        torch.cuda.synchronize()
+        assert guards_intact(big, g, out.numel(), b0) and guards_intact(lbig, lg, lse.numel(), l0)
+        assert torch.equal(out[1].view(torch.int16), b0[g:g + out.numel()].view(out.shape)[1].view(torch.int16))
+        ref, _ = oracle_full(inp, active=[1, 0, 1])
+        got = host_f64(out[[0, 2]])
+        assert_attn_close(got, ref[[0, 2]], "active")
+
+
+def sampled_rows(w, lens, n=24, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = {(0, 0, 0), (w.B - 1, w.S - 1, w.Hq - 1), (0, w.S - 1, w.Hq // 2), (w.B - 1, 0, 1)}
+    while len(rows) < n:
+        rows.add((int(rng.integers(w.B)), int(rng.integers(w.S)), int(rng.integers(w.Hq))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["decode", "batched16", "batched32", "long", "stress_a", "stress_b"])
+def test_official_workloads_full_size_sampled(name):
+    w = I.WORKLOADS[name]
+    print(f"[attn] full-size {name}", flush=True)
+    inp = I.attn_inputs(w)
+    got, lse, t = run_gpu(inp)
+    rows = sampled_rows(w, inp["prefix_len"], n=48 if name == "decode" else 24)
+    ref = O.attn_rows(inp["q"], inp["k_blk"], inp["v_blk"], inp["k_cache"], inp["v_cache"], inp["prefix_len"], rows)
+    g = np.stack([got[b, s, h] for (b, s, h) in rows])
+    r = np.stack([ref[k][0] for k in rows])
+    assert_attn_close(g, r, name)
+    np.testing.assert_allclose([lse[b, h, s] for (b, s, h) in rows], [ref[k][1] for k in rows], rtol=1e-4, atol=1e-3)
+    # the whole output is finite and the cache was not written
+    assert np.all(np.isfinite(got))
+    assert torch.equal(t["k_cache"].view(torch.int16).cpu(), torch.from_numpy(inp["k_cache"].view(np.int16)))

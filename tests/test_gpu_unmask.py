@@ -1,0 +1,126 @@
+"""GPU parity of bd_confidence_unmask against the float64 oracle (through the C ABI).
+
+Argmax ids, commit masks, tokens and commit counts must be bit-exact; confidences agree to float32
+rounding. The oracle's margin report must show no decision closer to gamma (or, for the
+fallback, to the runner-up) than 1e-4 relative: inside that band both answers are correct to
+within rounding, and the inputs are chosen so that none falls there."""
+import numpy as np
+import pytest
+import torch
+
+import block_diffusion_lm_amd as bd
+from block_diffusion_lm_amd import inputs as I
+from oracle import bd_oracle as O
+from tests.gpu_util import dev, dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def run_both(logits_host, is_bf16, mask, S, gamma, min_commit=True, commit_all=False, vocab=None, tokens=None):
+    B = mask.shape[0] // S
+    tokens = np.full(mask.shape[0], -5, np.int32) if tokens is None else tokens
+    lg = dev_bf16(logits_host) if is_bf16 else dev(logits_host)
+    m_d = dev(mask.copy())
+    t_d = dev(tokens.copy())
+    res = bd.confidence_unmask(lg, m_d, t_d, S, gamma, vocab=vocab, min_commit=min_commit, commit_all=commit_all)
+    torch.cuda.synchronize()
+    V = logits_host.shape[1] if vocab is None else vocab
+    host = logits_host[:, :V]
+    ref = O.confidence_unmask(host, mask, tokens, S, gamma, min_commit, commit_all,
+                              decode=O.bf16_to_f64 if is_bf16 else None)
+    nt = O.near_ties(ref["conf"], mask, S, gamma, min_commit, commit_all)
+    assert not nt, f"inputs have near-tie decisions: {nt[:4]}"
+    got = {"mask": m_d.cpu().numpy(), "tokens": t_d.cpu().numpy(), "n_commit": res["n_commit"].cpu().numpy(),
+           "conf": res["conf"].cpu().numpy(), "argmax": res["argmax"].cpu().numpy()}
+    np.testing.assert_array_equal(got["argmax"], ref["argmax"])
+    np.testing.assert_array_equal(got["mask"], ref["mask"])
+    np.testing.assert_array_equal(got["tokens"], ref["tokens"])
+    np.testing.assert_array_equal(got["n_commit"], ref["n_commit"])
+    np.testing.assert_allclose(got["conf"], ref["conf"], rtol=2e-5, atol=1e-30)
+    return got, ref
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "batched16", "batched32", "stress_a", "stress_b"])
+def test_official_workloads(name):
+    w = I.WORKLOADS[name]
+    print(f"[unmask] {name}", flush=True)
+    lg = I.logits(w)
+    mask = I.initial_mask(w)
+    got, ref = run_both(lg, w.logits_dtype == "bf16", mask, w.S, w.gamma)
+    if name == "stress_a" or name == "stress_b":
+        # the planted fallback tie of sequence 0: two identical rows, the earlier one commits
+        ms = np.flatnonzero(mask[: w.S])
+        if ref["n_commit"][0] == 1 and len(ms) >= 2 and ref["conf"][ms[0]] == ref["conf"][ms[-1]]:
+            assert got["mask"][ms[0]] == 0 and got["mask"][ms[-1]] == 1
+
+
+def test_long_workload_every_step():
+    w = I.WORKLOADS["long"]
+    mask = I.initial_mask(w)
+    tokens = np.zeros(w.B * w.S, np.int32)
+    for t in range(w.T):
+        if not mask.any():
+            break
+        got, ref = run_both(I.logits(w, t), True, mask, w.S, w.gamma, commit_all=(t == w.T - 1), tokens=tokens)
+        mask, tokens = ref["mask"], ref["tokens"]
+
+
+def test_additive_peak_recipe():
+    w = I.WORKLOADS["decode"]
+    run_both(I.logits(w, additive_peaks=True), True, I.initial_mask(w), w.S, w.gamma)
+
+
+@pytest.mark.parametrize("gamma,commit_all,min_commit", [(0.0, False, True), (1.0, False, True), (0.9, True, True),
+                                                         (0.9, False, False)])
+def test_special_rules(gamma, commit_all, min_commit):
+    w = I.small_workload("rules", B=5, S=16, V=40000, logits_dtype="bf16", sigma=3.0, ties=True, wid=240)
+    got, ref = run_both(I.logits(w), True, I.initial_mask(w), w.S, gamma, min_commit, commit_all)
+    if gamma == 1.0:
+        assert np.all(ref["n_commit"][I.initial_mask(w).reshape(5, 16).any(axis=1)] == 1)
+
+
+def test_ragged_vocab_padded_stride_and_neg_inf():
+    rng = np.random.default_rng(3)
+    V, stride, S, B = 1001, 1008, 8, 3
+    x = (rng.standard_normal((B * S, stride)) * 2).astype(np.float32)
+    x[:, V:] = 1e30          # padding past the vocabulary must never be read
+    x[0, :500] = -np.inf     # -inf logits are allowed (at least one finite value per row)
+    x[1, V - 1] = 50.0       # maximum in the ragged tail
+    x[2, 3] = x[2, 900] = 40.0   # tie across threads: lowest index wins
+    mask = np.ones(B * S, np.uint8)
+    mask[5] = 0
+    got, ref = run_both(x, False, mask, S, 0.6, vocab=V)   # row 2: two equal maxima -> p just under 0.5
+    assert got["argmax"][1] == V - 1 and got["argmax"][2] == 3 and got["argmax"][5] == -1
+
+
+def test_calibrated_rows_around_gamma():
+    # single peak delta over zeros: p = e^d / (e^d + V - 1); pick bf16 deltas just above and
+    # below the value where p = gamma, so the strict comparison is exercised on both sides.
+    V, S = 131072, 16
+    gamma = 0.9
+    d_star = np.log(gamma / (1 - gamma) * (V - 1))
+    grid = I.bf16_bits_to_f32(np.arange(0x4100, 0x4180, dtype=np.uint16)).astype(np.float64)
+    below = grid[grid < d_star].max()
+    above = grid[grid > d_star].min()
+    x = np.zeros((S, V), np.float32)
+    for s in range(S):
+        x[s, (s * 7919) % V] = above if s % 2 == 0 else below
+    got, ref = run_both(I.f32_to_bf16_bits(x), True, np.ones(S, np.uint8), S, gamma)
+    np.testing.assert_array_equal(got["mask"], [0 if s % 2 == 0 else 1 for s in range(S)])
+
+
+def test_determinism_identical_rows():
+    w = I.WORKLOADS["decode"]
+    lg = I.logits(w)
+    lg[5] = lg[2]
+    d = dev_bf16(lg)
+    mask = dev(np.ones(16, np.uint8))
+    confs = []
+    for _ in range(2):
+        m = mask.clone()
+        t = torch.zeros(16, dtype=torch.int32, device="cuda")
+        r = bd.confidence_unmask(d, m, t, 16, 0.9)
+        confs.append(r["conf"].clone())
+    torch.cuda.synchronize()
+    assert torch.equal(confs[0], confs[1])
+    assert confs[0][5].item() == confs[0][2].item()
