@@ -1,0 +1,255 @@
+"""Benchmark of the block-diffusion denoise step on one MI355X.
+
+A step is one pass of the whole hot path: one bd_denoise_block call that runs the T-step loop
+over a block -- per step the block+prefix attention (split and merge kernels), then the
+confidence unmasking (vocabulary reduction and commit kernels) -- on seeded synthetic inputs
+already resident in HBM.
+
+Default workload: the long-context loop -- B=4 sequences, 32 query / 2 KV heads, head_dim 128,
+block S=16, prefix L=65536, vocabulary 131072 (bf16 logits, planted peaks), T=8 steps, gamma=0.9,
+commit-at-least-one, every remaining position committed at the last step. Other workloads can be
+selected with --workload (single-step ones run T=1).
+
+Prints ONE JSON line. `value` is attention TFLOP/s over the whole step (all attention FLOPs the
+loop executes divided by the wall time of the loop, unmasking included); the per-kernel figures
+come from HIP events recorded around every kernel launch inside the timed region (libbd's
+kernel trace, on the launch stream). The CPU baseline times the float64 oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def attn_units(w, lens, active):
+    """Algorithmic work of one attention launch over the active sequences.
+
+    flops = sum_b 4 * Hq * S * (len_b + S) * D (Q K^T and P V);
+    kv_bytes = sum_b 2 * Hkv * (len_b + S) * D * 2 (prefix and block K and V, bf16, read once);
+    q_bytes = sum_b S * Hq * D * 2; o_bytes the same (written by the merge)."""
+    fl = kv = qb = 0
+    for b in range(w.B):
+        if not active[b]:
+            continue
+        n = int(lens[b]) + w.S
+        fl += 4 * w.Hq * w.S * n * w.D
+        kv += 2 * w.Hkv * n * w.D * 2
+        qb += w.S * w.Hq * w.D * 2
+    return fl, kv, qb
+
+
+def cpu_baseline(w, inputs, logits0, mask0, budget_s=20.0):
+    """Time the oracle as it stands on a bounded sample of the workload: the attention of
+    whole (sequence, KV head) groups of step 0 and the vocabulary reduction of masked rows."""
+    from oracle import bd_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    lens = inputs["prefix_len"]
+    t0 = time.perf_counter()
+    fl = 0
+    pairs = 0
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            rows = [(b, s, h) for s in range(w.S) for h in range(g * w.group, (g + 1) * w.group)]
+            O.attn_rows(inputs["q"], inputs["k_blk"], inputs["v_blk"], inputs["k_cache"], inputs["v_cache"], lens, rows)
+            fl += 4 * len(rows) * (int(lens[b]) + w.S) * w.D
+            pairs += 1
+            if time.perf_counter() - t0 > budget_s * 0.7:
+                break
+        if time.perf_counter() - t0 > budget_s * 0.7:
+            break
+    t_attn = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    masked = np.flatnonzero(mask0)
+    dec = O.bf16_to_f64 if w.logits_dtype == "bf16" else None
+    n = 0
+    for r in masked:
+        O.confidences(logits0[r:r + 1], np.ones(1, np.uint8), dec)
+        n += 1
+        if time.perf_counter() - t1 > budget_s * 0.3:
+            break
+    t_um = time.perf_counter() - t1
+    return {"value": fl / t_attn / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 oracle: attention of {pairs} (sequence, KV head) groups "
+                      f"({pairs * w.S * w.group} query rows over {int(lens[0]) + w.S} keys) in {t_attn:.1f} s; "
+                      f"vocabulary reduction of {n} masked rows in {t_um:.2f} s",
+            "unmask_positions_per_s": n / t_um if t_um > 0 else None}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--sets", type=int, default=3, help="independent prefix caches rotated between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X (no multi-GPU path); "
+              "use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_diffusion_lm_amd as bd
+    from block_diffusion_lm_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    T = w.T
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    print(f"[bench] generating inputs for {w.name}", file=sys.stderr, flush=True)
+    lens = I.prefix_lengths(w)
+    inp0 = I.attn_inputs(w, step=0, lens=lens)
+    steps = [I.attn_inputs(w, step=t, lens=lens, cache=False) if t else inp0 for t in range(T)]
+    dq = [tuple(d16(steps[t][k]) for k in ("q", "k_blk", "v_blk")) for t in range(T)]
+    logits_np = [I.logits(w, step=t) for t in range(T)]
+    is_bf16 = w.logits_dtype == "bf16"
+    dlog = [d16(x) if is_bf16 else torch.from_numpy(x).to(dev) for x in logits_np]
+    mask0 = I.initial_mask(w)
+    caches = [(d16(inp0["k_cache"]), d16(inp0["v_cache"]))]
+    g = torch.Generator(device=dev)
+    g.manual_seed(20261203)
+    for _ in range(1, args.sets):   # same distribution (bf16 N(0,1)), distinct bytes
+        caches.append(tuple(torch.randn(inp0["k_cache"].shape, generator=g, device=dev).to(torch.bfloat16)
+                            for _ in range(2)))
+    lens_d = torch.from_numpy(lens).to(dev)
+    mask_d = torch.from_numpy(mask0).to(dev)
+    tok_d = torch.zeros(w.B * w.S, dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.S, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+
+    ad = bd.attn_desc(w.B, w.Hq, w.Hkv, w.D, w.S, inp0["k_cache"].shape[2], w.max_prefix_len)
+    ud = bd.unmask_desc(w.B, w.S, w.V, None, is_bf16, w.gamma, True, False)
+    ws = torch.empty(max(bd.denoise_workspace_bytes(ad, ud), 1), dtype=torch.uint8, device=dev)
+
+    table = ([x[0] for x in dq], [x[1] for x in dq], [x[2] for x in dq], dlog)
+    steps_used_d = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    cps_d = torch.zeros((T, w.B), dtype=torch.int32, device=dev)
+
+    def step(i):
+        kc, vc = caches[i % len(caches)]
+        mask_d.copy_(mask_src)   # every step denoises the same fresh block
+        return bd.denoise_block(None, None, kc, vc, lens_d, mask_d, tok_d, T, w.Hq, w.gamma, w.S, w.V,
+                                logits_bf16=is_bf16, out=out, workspace=ws, step_table=table,
+                                steps_used=steps_used_d, commits_per_step=cps_d)
+
+    mask_src = torch.from_numpy(mask0).to(dev)
+    for i in range(args.warmup):
+        r = step(i)
+    torch.cuda.synchronize()
+    steps_used = r["steps_used"].cpu().numpy()
+    commits = r["commits_per_step"].cpu().numpy()
+
+    # the mask reset (a 64-byte device copy) is part of every iteration; it is not a library kernel
+    trace = bd.Trace(capacity=args.steps * (4 * T + 1) + 16)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with trace:
+        for i in range(args.steps):
+            step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    recs = trace.records()
+    trace.close()
+
+    # control flow is deterministic: sequences active at step t are those with steps_used > t
+    per_kernel = {}
+    for name, ms in recs:
+        per_kernel.setdefault(name, []).append(ms)
+    split_ms = per_kernel.get("attn_split", [])
+    merge_ms = per_kernel.get("attn_merge", [])
+    red_ms = per_kernel.get("vocab_reduce", [])
+    com_ms = per_kernel.get("commit", [])
+    fl_step = kv_step = q_step = 0
+    masked_rows_step = 0
+    m = mask0.reshape(w.B, w.S).copy()
+    per_launch_bytes = []
+    for t in range(T):
+        active = steps_used > t
+        fl, kv, qb = attn_units(w, lens, active)
+        fl_step += fl
+        kv_step += kv
+        q_step += qb
+        per_launch_bytes.append(kv + qb)
+    # masked rows read by the vocabulary reduction, step by step (from the commit counts)
+    remaining = mask0.reshape(w.B, w.S).sum(axis=1).astype(np.int64)
+    for t in range(T):
+        masked_rows_step += int(remaining.sum())
+        remaining -= commits[t]
+    K = args.steps
+    ms_per_step = wall / K * 1e3
+    attn_ms = (sum(split_ms) + sum(merge_ms)) / K
+    unmask_ms = (sum(red_ms) + sum(com_ms)) / K
+    split_avg = float(np.mean(split_ms))
+    bytes_per_launch = float(np.mean(per_launch_bytes))
+    achieved_gbs = bytes_per_launch / (split_avg * 1e-3) / 1e9
+    value = fl_step / (ms_per_step * 1e-3) / 1e12
+    line = {
+        "metric": "denoise-step attn TFLOP/s & KV GB/s (% roofline); unmask positions/s",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: denoise loop B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} S={w.S} "
+                               f"L={w.prefix_len} V={w.V} T={T} gamma={w.gamma}",
+                   "global_batch": w.B, "block_len": w.S, "prefix_len": w.max_prefix_len, "T": T,
+                   "vocab": w.V, "parallelism": "none (1 GPU)"},
+        "attention": {
+            "ms_per_step": round(attn_ms, 4),
+            "tflops": round(fl_step / (attn_ms * 1e-3) / 1e12, 3),
+            "tflops_frac_bf16_peak": round(fl_step / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "kv_gbs": round(kv_step / (attn_ms * 1e-3) / 1e9, 1),
+            "kv_frac_hbm_peak": round(kv_step / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "split_avg_ms": round(split_avg, 5),
+            "merge_avg_ms": round(float(np.mean(merge_ms)), 5) if merge_ms else 0.0,
+        },
+        "unmask": {
+            "ms_per_step": round(unmask_ms, 4),
+            "positions_per_s": round(masked_rows_step / (unmask_ms * 1e-3), 1),
+            "frac_roofline": round(masked_rows_step / (unmask_ms * 1e-3) / (HBM_PEAK_GBS * 1e9 / (w.V * (2 if is_bf16 else 4))), 4),
+            "reduce_avg_ms": round(float(np.mean(red_ms)), 5),
+        },
+        "loop": {"steps_used": steps_used.tolist(), "commits_per_step": commits.sum(axis=1).tolist(),
+                 "tokens_per_step": round(float(mask0.sum()) / max(1, int(steps_used.max())), 3)},
+        "roofline": {"kernel": "attn_split", "bound": "hbm", "achieved": round(achieved_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, inp0, logits_np[0], mask0, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -142,14 +142,17 @@ def confidence_unmask(logits, mask, tokens, block_len, gamma, vocab=None, min_co
     return {"conf": conf, "argmax": argmax, "n_commit": n_commit}
 
 
-def denoise_block(get_qkv: Callable, get_logits: Callable, k_cache, v_cache, prefix_len, mask, tokens, T: int,
+def denoise_block(get_qkv: Optional[Callable], get_logits: Optional[Callable], k_cache, v_cache, prefix_len, mask,
+                  tokens, T: int,
                   Hq: int, gamma: float, block_len: int, vocab: int, logits_bf16: bool = True, row_stride=None,
                   t0: int = 0, min_commit=True, max_prefix_len=None, softmax_scale=0.0, num_splits=0, out=None,
-                  commits_per_step=True, workspace=None, stream=None):
-    """bd_denoise_block with Python hooks.
+                  commits_per_step=True, workspace=None, stream=None, step_table=None, steps_used=None):
+    """bd_denoise_block.
 
-    ``get_qkv(step, mask, tokens) -> (q, k_blk, v_blk)`` and ``get_logits(step, out) -> logits``
-    return device tensors (kept alive by this function until the next hook call). Returns
+    Either Python hooks -- ``get_qkv(step, mask, tokens) -> (q, k_blk, v_blk)`` and
+    ``get_logits(step, out) -> logits`` returning device tensors (kept alive until the next hook
+    call) -- or ``step_table = (qs, k_blks, v_blks, logits)``: per-step tensor lists replayed by
+    the library's native table hooks (no call back into Python). Returns
     dict(out, steps_used, commits_per_step)."""
     torch = _torch()
     L = _lib.load()
@@ -164,8 +167,14 @@ def denoise_block(get_qkv: Callable, get_logits: Callable, k_cache, v_cache, pre
     ud = unmask_desc(B, S, vocab, row_stride, logits_bf16, gamma, min_commit, False)
     if out is None:
         out = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=k_cache.device)
-    steps_used = torch.empty(B, dtype=torch.int32, device=k_cache.device)
-    cps = torch.zeros((T, B), dtype=torch.int32, device=k_cache.device) if commits_per_step else None
+    if steps_used is None:
+        steps_used = torch.empty(B, dtype=torch.int32, device=k_cache.device)
+    if commits_per_step is True:
+        cps = torch.zeros((T, B), dtype=torch.int32, device=k_cache.device)
+    elif commits_per_step is False or commits_per_step is None:
+        cps = None
+    else:
+        cps = commits_per_step
     nbytes = L.bd_denoise_workspace_bytes(ctypes.byref(ad), ctypes.byref(ud))
     ws = _workspace(nbytes, k_cache.device, workspace)
     keep = {}
@@ -191,7 +200,18 @@ def denoise_block(get_qkv: Callable, get_logits: Callable, k_cache, v_cache, pre
             errors.append(e)
             return _lib.BD_EINVAL
 
-    hooks = StepHooks(_lib.GET_QKV(_qkv), _lib.GET_LOGITS(_logits), None)
+    if step_table is not None:
+        qs, ks, vs, ls = step_table
+        if not (len(qs) == len(ks) == len(vs) == len(ls) >= T):
+            raise ValueError("step_table needs T entries per list")
+        arr = lambda ts: (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+        keep["table"] = (arr(qs), arr(ks), arr(vs), arr(ls))
+        table = _lib.StepTable(*[ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)) for a in keep["table"]], len(qs))
+        keep["tab"] = table
+        hooks = StepHooks()
+        _lib.check(L.bd_table_hooks(ctypes.byref(table), ctypes.byref(hooks)), "bd_table_hooks")
+    else:
+        hooks = StepHooks(_lib.GET_QKV(_qkv), _lib.GET_LOGITS(_logits), None)
     st = L.bd_denoise_block(ctypes.byref(ad), ctypes.byref(ud), T, t0, ctypes.byref(hooks), _ptr(k_cache),
                             _ptr(v_cache), _ptr(prefix_len), _ptr(out), _ptr(mask), _ptr(tokens), _ptr(steps_used),
                             _ptr(cps), _ptr(ws), ws.numel(), _stream(stream))

@@ -50,10 +50,16 @@ class StepHooks(ctypes.Structure):
     _fields_ = [("get_qkv", GET_QKV), ("get_logits", GET_LOGITS), ("user", ctypes.c_void_p)]
 
 
+class StepTable(ctypes.Structure):
+    _fields_ = [("q", ctypes.POINTER(ctypes.c_void_p)), ("k_blk", ctypes.POINTER(ctypes.c_void_p)),
+                ("v_blk", ctypes.POINTER(ctypes.c_void_p)), ("logits", ctypes.POINTER(ctypes.c_void_p)),
+                ("n_steps", ctypes.c_int32)]
+
+
 EXPORTS = [
     "bd_attn_workspace_bytes", "bd_attn_step", "bd_unmask_workspace_bytes", "bd_confidence_unmask",
     "bd_denoise_workspace_bytes", "bd_denoise_block", "bd_last_error", "bd_trace_create", "bd_trace_destroy",
-    "bd_trace_attach", "bd_trace_clear", "bd_trace_count", "bd_trace_get", "bd_version",
+    "bd_trace_attach", "bd_trace_clear", "bd_trace_count", "bd_trace_get", "bd_version", "bd_table_hooks",
 ]
 
 _lib = None
@@ -85,6 +91,8 @@ def load() -> ctypes.CDLL:
     L.bd_denoise_block.argtypes = [P(AttnDesc), P(UnmaskDesc), i32, i32, P(StepHooks), vp, vp, vp, vp, vp, vp, vp,
                                    vp, vp, sz, vp]
     L.bd_denoise_block.restype = ctypes.c_int
+    L.bd_table_hooks.argtypes = [P(StepTable), P(StepHooks)]
+    L.bd_table_hooks.restype = ctypes.c_int
     L.bd_last_error.argtypes = []
     L.bd_last_error.restype = ctypes.c_char_p
     L.bd_version.argtypes = []

@@ -88,8 +88,11 @@ void plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
   const int group = d->n_q_heads / d->n_kv_heads;
   p->head_dim = d->head_dim;
   p->rows = d->block_len * group;
-  p->waves = p->rows <= 64 ? 1 : p->rows <= 128 ? 2 : 4;
-  const int tile_rows = p->waves * bd::kRowsPerWave;
+  // 32 query rows per wave, two waves per SIMD: the hardware interleaves one wave's MFMAs with
+  // the other's softmax. Eight waves share each LDS key tile when the group has > 128 rows.
+  p->rows_per_wave = 32;
+  p->waves = p->rows > 128 ? 8 : 4;
+  const int tile_rows = p->waves * p->rows_per_wave;
   p->row_tiles = (p->rows + tile_rows - 1) / tile_rows;
   const int64_t nkeys = d->max_prefix_len + d->block_len;
   const int64_t base = (int64_t)d->batch * d->n_kv_heads * p->row_tiles;
@@ -99,7 +102,7 @@ void plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
   } else {
     // fill every workgroup slot of the chip once, without chunks shorter than kMinChunk keys
     const size_t lds = 2 * ((size_t)bd::kKeyTile * (d->head_dim * 2 + 16) + (size_t)d->head_dim * bd::kKeyTile * 2);
-    const int by_regs = 4 / p->waves;
+    const int by_regs = (p->rows_per_wave == 64 ? 4 : 8) / p->waves;
     const int by_lds = (int)(kLdsPerCU / lds);
     const int64_t slots = (int64_t)kCUs * (by_regs < by_lds ? by_regs : by_lds);
     nsplit = (slots + base - 1) / base;
@@ -113,6 +116,7 @@ void plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
   p->nsplit = (int)((nkeys + chunk - 1) / chunk);
   p->n_items = base * p->nsplit;
   p->direct = p->nsplit == 1;
+  p->wide_merge = p->nsplit > 16;
   if (p->direct) {
     p->part_acc_off = p->part_ml_off = p->bytes = 0;
   } else {
@@ -161,9 +165,10 @@ bd_status run_attn(const bd_attn_desc* d, const bd::AttnPlan& plan, const void* 
   a.Hkv = d->n_kv_heads;
   a.group = d->n_q_heads / d->n_kv_heads;
   a.rows = plan.rows;
-  a.rows_pad = plan.waves * bd::kRowsPerWave;
+  a.rows_pad = plan.waves * plan.rows_per_wave;
   a.lcap = d->prefix_capacity;
   a.chunk = plan.chunk;
+  a.max_keys = d->max_prefix_len + d->block_len;
   a.nsplit = plan.nsplit;
   a.row_tiles = plan.row_tiles;
   const float tau = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
@@ -371,6 +376,32 @@ bd_status bd_denoise_block(const bd_attn_desc* attn, const bd_unmask_desc* unmas
   return BD_OK;
 }
 
+static bd_status table_get_qkv(void* user, int32_t step, const uint8_t*, const int32_t*, const void** q,
+                               const void** kb, const void** vb, void*) {
+  const bd_step_table* t = static_cast<const bd_step_table*>(user);
+  if (!t || step < 0 || step >= t->n_steps) return fail(BD_EINVAL, "step %d outside the step table", step);
+  *q = t->q[step];
+  *kb = t->k_blk[step];
+  *vb = t->v_blk[step];
+  return BD_OK;
+}
+
+static bd_status table_get_logits(void* user, int32_t step, const void*, const void** logits, void*) {
+  const bd_step_table* t = static_cast<const bd_step_table*>(user);
+  if (!t || step < 0 || step >= t->n_steps) return fail(BD_EINVAL, "step %d outside the step table", step);
+  *logits = t->logits[step];
+  return BD_OK;
+}
+
+bd_status bd_table_hooks(const bd_step_table* table, bd_step_hooks* hooks_out) {
+  if (!table || !hooks_out || !table->q || !table->k_blk || !table->v_blk || !table->logits || table->n_steps < 1)
+    return fail(BD_EINVAL, "bd_table_hooks: incomplete step table");
+  hooks_out->get_qkv = table_get_qkv;
+  hooks_out->get_logits = table_get_logits;
+  hooks_out->user = const_cast<bd_step_table*>(table);
+  return BD_OK;
+}
+
 // ------------------------------------------------------------------------------------------
 // tracing
 // ------------------------------------------------------------------------------------------
@@ -393,8 +424,8 @@ void bd_trace_destroy(bd_trace* t) {
   if (!t) return;
   if (g_trace == t) g_trace = nullptr;
   for (auto& r : t->recs) {
-    if (r.start) hipEventDestroy(r.start);
-    if (r.stop) hipEventDestroy(r.stop);
+    if (r.start) (void)hipEventDestroy(r.start);
+    if (r.stop) (void)hipEventDestroy(r.stop);
   }
   delete t;
 }

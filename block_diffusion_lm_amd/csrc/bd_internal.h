@@ -11,18 +11,19 @@ namespace bd {
 // ---------------------------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------------------------
-constexpr int kRowsPerWave = 64;   // two 32-row MFMA blocks per wave
 constexpr int kKeyTile = 64;       // keys staged through LDS per iteration
 
 struct AttnPlan {
   int head_dim;       // D
-  int waves;          // waves per workgroup (1, 2 or 4); a workgroup owns waves*64 query rows
+  int waves;          // waves per workgroup (1, 2, 4 or 8)
+  int rows_per_wave;  // 32 or 64 (one or two 32-row MFMA blocks); a workgroup owns waves*rows_per_wave rows
   int rows;           // R = S * (Hq / Hkv): query rows per (sequence, KV head)
-  int row_tiles;      // ceil(R / (waves * 64))
+  int row_tiles;      // ceil(R / (waves * rows_per_wave))
   int64_t chunk;      // keys per split (multiple of kKeyTile)
   int nsplit;         // splits per (sequence, KV head)
   int64_t n_items;    // B * Hkv * nsplit * row_tiles workgroups
   bool direct;        // nsplit == 1: the split kernel writes the final output itself
+  bool wide_merge;    // many splits: merge with one workgroup per query row
   size_t part_acc_off, part_ml_off, bytes;   // workspace layout
 };
 
@@ -41,6 +42,7 @@ struct AttnArgs {
   int B, S, Hq, Hkv, group, rows, rows_pad;
   int64_t lcap;
   int64_t chunk;
+  int64_t max_keys;   // max_prefix_len + S: the longest key sequence the plan covers
   int nsplit, row_tiles;
   float scale_log2;   // tau * log2(e)
   int direct;

@@ -163,6 +163,20 @@ typedef struct {
   void* user;
 } bd_step_hooks;
 
+/* Hooks that replay precomputed per-step device pointers (no host callback into the caller).
+ * step t uses q[t], k_blk[t], v_blk[t] and logits[t]; the table (host arrays of n_steps device
+ * pointers each) must stay alive while the loop is being enqueued. A step outside
+ * [0, n_steps) makes the hook return BD_EINVAL. */
+typedef struct {
+  const void* const* q;
+  const void* const* k_blk;
+  const void* const* v_blk;
+  const void* const* logits;
+  int32_t n_steps;
+} bd_step_table;
+
+bd_status bd_table_hooks(const bd_step_table* table, bd_step_hooks* hooks_out);
+
 size_t bd_denoise_workspace_bytes(const bd_attn_desc* attn, const bd_unmask_desc* unmask);
 
 /* attn / unmask: descriptors as above (unmask->commit_all is ignored; the loop sets it).

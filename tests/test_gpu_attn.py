@@ -12,7 +12,7 @@ import torch
 import block_diffusion_lm_amd as bd
 from block_diffusion_lm_amd import inputs as I
 from oracle import bd_oracle as O
-from tests.gpu_util import assert_attn_close, bf16_f64, dev, dev_bf16, guarded, guards_intact, host_f64
+from tests.gpu_util import LSE_ATOL, assert_attn_close, bf16_f64, dev, dev_bf16, guarded, guards_intact, host_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +53,7 @@ def test_small_shapes_match_oracle(case, num_splits):
     got, lse, _ = run_gpu(inp, num_splits=num_splits)
     ref, ref_lse = oracle_full(inp)
     assert_attn_close(got, ref, name)
-    np.testing.assert_allclose(lse, ref_lse, rtol=1e-4, atol=1e-3)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
 
 
 def test_tiny_workload_and_planted_large_scores():
@@ -62,7 +62,7 @@ def test_tiny_workload_and_planted_large_scores():
     got, lse, _ = run_gpu(inp)
     ref, ref_lse = oracle_full(inp)
     assert_attn_close(got, ref, "tiny")
-    np.testing.assert_allclose(lse, ref_lse, rtol=1e-4, atol=1e-3)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
     # planted large scores: one prefix key per KV head aligned with every query -> O ~ its V row (O(1))
     inp2 = {k: v.copy() for k, v in inp.items()}
     qf = bf16_f64(inp2["q"])
@@ -144,7 +144,7 @@ def test_official_workloads_full_size_sampled(name):
     g = np.stack([got[b, s, h] for (b, s, h) in rows])
     r = np.stack([ref[k][0] for k in rows])
     assert_attn_close(g, r, name)
-    np.testing.assert_allclose([lse[b, h, s] for (b, s, h) in rows], [ref[k][1] for k in rows], rtol=1e-4, atol=1e-3)
+    np.testing.assert_allclose([lse[b, h, s] for (b, s, h) in rows], [ref[k][1] for k in rows], rtol=0, atol=LSE_ATOL)
     # the whole output is finite and the cache was not written
     assert np.all(np.isfinite(got))
     assert torch.equal(t["k_cache"].view(torch.int16).cpu(), torch.from_numpy(inp["k_cache"].view(np.int16)))

@@ -115,3 +115,26 @@ def test_long_workload_full_loop():
 
     res, ref = run_loop(w, full_oracle=False, sample_rows=rows)
     assert ref["steps_used"].max() >= 2      # the loop runs several steps before every position commits
+
+
+def test_native_step_table_matches_python_hooks():
+    w = I.small_workload("loop3", B=2, Hq=32, Hkv=2, D=128, S=16, prefix_len=(300, 1200), V=2048, logits_dtype="bf16",
+                         sigma=3.0, gamma=0.9, mask_rule="all", peaks=True, T=4, wid=252)
+    lens = I.prefix_lengths(w)
+    cache = I.prefix_cache(w, lens)
+    steps = [I.attn_inputs(w, step=t, lens=lens, cache=False) for t in range(w.T)]
+    qkv = [tuple(dev_bf16(steps[t][k]) for k in ("q", "k_blk", "v_blk")) for t in range(w.T)]
+    lg = [dev_bf16(I.logits(w, step=t)) for t in range(w.T)]
+    kc, vc, ln = dev_bf16(cache["k_cache"]), dev_bf16(cache["v_cache"]), dev(lens)
+    results = []
+    for mode in ("python", "table"):
+        m_d, t_d = dev(I.initial_mask(w)), dev(np.zeros(w.B * w.S, np.int32))
+        kw = {"step_table": ([x[0] for x in qkv], [x[1] for x in qkv], [x[2] for x in qkv], lg)} if mode == "table" else {}
+        res = bd.denoise_block((lambda t, m, tk: qkv[t]) if mode == "python" else None,
+                               (lambda t, o: lg[t]) if mode == "python" else None,
+                               kc, vc, ln, m_d, t_d, w.T, w.Hq, w.gamma, w.S, w.V, **kw)
+        torch.cuda.synchronize()
+        results.append((m_d.cpu(), t_d.cpu(), res["steps_used"].cpu(), res["commits_per_step"].cpu(),
+                        res["out"].view(torch.int16).cpu()))
+    for a, b in zip(*results):
+        assert torch.equal(a, b)
