@@ -92,6 +92,23 @@ def cpu_baseline(w, inputs, logits0, mask0, budget_s=20.0):
             "unmask_positions_per_s": n / t_um if t_um > 0 else None}
 
 
+def measured_traffic(kernel_source: str):
+    """HBM traffic per launch of the attention split kernel from the committed counter summary
+    (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a plain copy kernel), or None when the summary
+    is missing or was taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_split_long_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(kernel_source, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +118,8 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="independent prefix caches rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device copy (5 times): the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build runs on a single MI355X (no multi-GPU path); "
@@ -108,6 +127,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": 512 << 20,
+                          "bytes_written_per_launch": 512 << 20}))
+        return
 
     import block_diffusion_lm_amd as bd
     from block_diffusion_lm_amd import inputs as I
@@ -162,16 +191,24 @@ def main():
     steps_used = r["steps_used"].cpu().numpy()
     commits = r["commits_per_step"].cpu().numpy()
 
-    # the mask reset (a 64-byte device copy) is part of every iteration; it is not a library kernel
-    trace = bd.Trace(capacity=args.steps * (4 * T + 1) + 16)
+    # Timed region: K steps, no tracing (the per-step mask reset, a 64-byte device copy, is part of
+    # every step). A second region of K steps runs with libbd's kernel trace attached: HIP events
+    # recorded around every kernel launch on the launch stream give the per-kernel durations.
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    trace = bd.Trace(capacity=args.steps * (4 * T + 1) + 16)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     with trace:
         for i in range(args.steps):
             step(i)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_traced = time.perf_counter() - t1
     recs = trace.records()
     trace.close()
 
@@ -215,6 +252,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_traced": round(wall_traced / K * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -243,7 +281,8 @@ def main():
                  "tokens_per_step": round(float(mask0.sum()) / max(1, int(steps_used.max())), 3)},
         "roofline": {"kernel": "attn_split", "bound": "hbm", "achieved": round(achieved_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(os.path.join(ROOT, "block_diffusion_lm_amd", "csrc", "bd_attn.hip")),
+                     "algorithmic_bytes_per_launch": round(bytes_per_launch)},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

@@ -43,6 +43,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr int kCUs = 256;                  // MI355X compute units
 constexpr size_t kLdsPerCU = 160 * 1024;   // bytes of LDS per compute unit
 constexpr int64_t kMinChunk = 512;         // keys per split below which splitting does not pay
+constexpr int kKeyTile = 64;               // keys per LDS tile of the attention kernel
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -92,6 +93,7 @@ void plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
   // the other's softmax. Eight waves share each LDS key tile when the group has > 128 rows.
   p->rows_per_wave = 32;
   p->waves = p->rows > 128 ? 8 : 4;
+  p->key_tile = kKeyTile;
   const int tile_rows = p->waves * p->rows_per_wave;
   p->row_tiles = (p->rows + tile_rows - 1) / tile_rows;
   const int64_t nkeys = d->max_prefix_len + d->block_len;
@@ -101,7 +103,7 @@ void plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
     nsplit = d->num_splits;
   } else {
     // fill every workgroup slot of the chip once, without chunks shorter than kMinChunk keys
-    const size_t lds = 2 * ((size_t)bd::kKeyTile * (d->head_dim * 2 + 16) + (size_t)d->head_dim * bd::kKeyTile * 2);
+    const size_t lds = 2 * ((size_t)p->key_tile * (d->head_dim * 2 + 16) + (size_t)d->head_dim * p->key_tile * 2);
     const int by_regs = (p->rows_per_wave == 64 ? 4 : 8) / p->waves;
     const int by_lds = (int)(kLdsPerCU / lds);
     const int64_t slots = (int64_t)kCUs * (by_regs < by_lds ? by_regs : by_lds);
@@ -111,7 +113,7 @@ void plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
     if (nsplit < 1) nsplit = 1;
   }
   int64_t chunk = (nkeys + nsplit - 1) / nsplit;
-  chunk = (chunk + bd::kKeyTile - 1) / bd::kKeyTile * bd::kKeyTile;
+  chunk = (chunk + 63) / 64 * 64;
   p->chunk = chunk;
   p->nsplit = (int)((nkeys + chunk - 1) / chunk);
   p->n_items = base * p->nsplit;
@@ -253,6 +255,11 @@ bd_status run_unmask(const bd_unmask_desc* d, const bd::UnmaskPlan& plan, const 
   return traced("commit", stream, [&] { return bd::launch_commit(a, stream); });
 }
 
+// denoise-loop workspace: [attention partials][unmask partials][active flags]
+size_t loop_bytes(const bd::AttnPlan& ap, const bd::UnmaskPlan& up, int B) {
+  return ap.bytes + up.bytes + align_up((size_t)B, 256);
+}
+
 bd_status check_ws(void* ws, size_t have, size_t need) {
   if (have < need) return fail(BD_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", have, need);
   if (need && !ws) return fail(BD_EINVAL, "workspace is NULL");
@@ -319,7 +326,7 @@ size_t bd_denoise_workspace_bytes(const bd_attn_desc* attn, const bd_unmask_desc
   bd::UnmaskPlan up;
   plan_attn(attn, &ap);
   plan_unmask(unmask, &up);
-  return ap.bytes + up.bytes + align_up((size_t)attn->batch, 256);
+  return loop_bytes(ap, up, attn->batch);
 }
 
 bd_status bd_denoise_block(const bd_attn_desc* attn, const bd_unmask_desc* unmask, int32_t T, int32_t t0,
@@ -345,7 +352,7 @@ bd_status bd_denoise_block(const bd_attn_desc* attn, const bd_unmask_desc* unmas
   bd::UnmaskPlan up;
   plan_attn(attn, &ap);
   plan_unmask(unmask, &up);
-  const size_t need = ap.bytes + up.bytes + align_up((size_t)attn->batch, 256);
+  const size_t need = loop_bytes(ap, up, attn->batch);
   st = check_ws(workspace, workspace_bytes, need);
   if (st != BD_OK) return st;
   char* w = static_cast<char*>(workspace);

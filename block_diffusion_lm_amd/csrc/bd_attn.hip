@@ -81,7 +81,7 @@ __device__ __forceinline__ ItemMap device_plan(const AttnArgs& a, int n_act) {
   const int64_t nkeys = a.max_keys;
   const int64_t ns = ((int64_t)a.nsplit * a.B) / n_act;
   int64_t chunk = (nkeys + ns - 1) / ns;
-  chunk = (chunk + kKeyTile - 1) / kKeyTile * kKeyTile;
+  chunk = (chunk + 63) / 64 * 64;
   m.chunk = chunk;
   m.nsplit = (int)((nkeys + chunk - 1) / chunk);
   return m;
@@ -108,9 +108,10 @@ __device__ __forceinline__ int rank_active(const uint8_t* active, int b) {
   return r;
 }
 
-template <int D>
+template <int D, int KT_>
 struct Geo {
-  static constexpr int KT = kKeyTile;
+  static constexpr int KT = KT_;                    // keys per LDS tile
+  static constexpr int KB = KT / 32;                // 32-key blocks per tile
   static constexpr int KROW = D * 2 + 16;          // bytes per key row of the K tile (padded)
   static constexpr int VROW = KT * 2;               // bytes per dim row of the transposed V tile
   static constexpr int KBYTES = KT * KROW;
@@ -126,9 +127,9 @@ struct Geo {
 __device__ __forceinline__ int vt_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
 
 // RB == 1 variants hold half the registers and are meant to run two waves per SIMD.
-template <int D, int NW, int RB>
+template <int D, int NW, int RB, int KT>
 __global__ __launch_bounds__(NW * 64, (RB == 1 && NW < 8) ? 8 / NW : 1) void attn_split_kernel(AttnArgs a) {
-  using G = Geo<D>;
+  using G = Geo<D, KT>;
   constexpr int NT = NW * 64;
   constexpr int D8 = D / 8;
   constexpr int ROWS_W = 32 * RB;                    // query rows per wave
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(NW * 64, (RB == 1 && NW < 8) ? 8 / NW : 1) void att
     const int valid = (int)min((int64_t)G::KT, k_end - kt0);   // keys of this tile inside the chunk
 
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < G::KB; ++kb) {
       if (kb * 32 >= valid) break;
       // ---- S^T = K Q^T for 32 keys: sacc[rb], 32 keys x 32 rows each
       if constexpr (kPrioMode == 2) __builtin_amdgcn_s_setprio(1);
@@ -563,7 +564,10 @@ __global__ __launch_bounds__(256) void attn_merge_wide_kernel(AttnArgs a, int ti
 
 template <int D, int NW, int RB>
 hipError_t launch_split_t(const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_split_kernel<D, NW, RB>), dim3((unsigned)plan.n_items), dim3(NW * 64), 0, stream, a);
+  if (plan.key_tile == 128)
+    hipLaunchKernelGGL((attn_split_kernel<D, NW, RB, 128>), dim3((unsigned)plan.n_items), dim3(NW * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<D, NW, RB, 64>), dim3((unsigned)plan.n_items), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -573,21 +577,13 @@ hipError_t launch_attn_split(const AttnPlan& plan, const AttnArgs& a, hipStream_
   const int key = plan.waves * 100 + plan.rows_per_wave;
   if (plan.head_dim == 128) {
     switch (key) {
-      case 164: return launch_split_t<128, 1, 2>(plan, a, stream);
-      case 264: return launch_split_t<128, 2, 2>(plan, a, stream);
       case 464: return launch_split_t<128, 4, 2>(plan, a, stream);
-      case 132: return launch_split_t<128, 1, 1>(plan, a, stream);
-      case 232: return launch_split_t<128, 2, 1>(plan, a, stream);
       case 432: return launch_split_t<128, 4, 1>(plan, a, stream);
       case 832: return launch_split_t<128, 8, 1>(plan, a, stream);
     }
   } else if (plan.head_dim == 64) {
     switch (key) {
-      case 164: return launch_split_t<64, 1, 2>(plan, a, stream);
-      case 264: return launch_split_t<64, 2, 2>(plan, a, stream);
       case 464: return launch_split_t<64, 4, 2>(plan, a, stream);
-      case 132: return launch_split_t<64, 1, 1>(plan, a, stream);
-      case 232: return launch_split_t<64, 2, 1>(plan, a, stream);
       case 432: return launch_split_t<64, 4, 1>(plan, a, stream);
       case 832: return launch_split_t<64, 8, 1>(plan, a, stream);
     }

@@ -11,7 +11,6 @@ namespace bd {
 // ---------------------------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------------------------
-constexpr int kKeyTile = 64;       // keys staged through LDS per iteration
 
 struct AttnPlan {
   int head_dim;       // D
@@ -19,7 +18,8 @@ struct AttnPlan {
   int rows_per_wave;  // 32 or 64 (one or two 32-row MFMA blocks); a workgroup owns waves*rows_per_wave rows
   int rows;           // R = S * (Hq / Hkv): query rows per (sequence, KV head)
   int row_tiles;      // ceil(R / (waves * rows_per_wave))
-  int64_t chunk;      // keys per split (multiple of kKeyTile)
+  int key_tile;       // keys staged through LDS per iteration (64 or 128)
+  int64_t chunk;      // keys per split (multiple of 64)
   int nsplit;         // splits per (sequence, KV head)
   int64_t n_items;    // B * Hkv * nsplit * row_tiles workgroups
   bool direct;        // nsplit == 1: the split kernel writes the final output itself

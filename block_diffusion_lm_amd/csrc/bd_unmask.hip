@@ -86,10 +86,16 @@ __device__ __forceinline__ float load_logit(const void* row, int is_bf16, int64_
   return reinterpret_cast<const float*>(row)[j];
 }
 
+__device__ void reduce_slice(const UnmaskArgs& a, int64_t row, int part);
+__device__ void commit_sequence(const UnmaskArgs& a, int b);
+
 __global__ __launch_bounds__(256) void vocab_reduce_kernel(UnmaskArgs a) {
   const int64_t row = blockIdx.x / a.vsplit;
   const int part = (int)(blockIdx.x % a.vsplit);
-  if (!a.mask[row]) return;
+  if (a.mask[row]) reduce_slice(a, row, part);   // uniform per workgroup
+}
+
+__device__ void reduce_slice(const UnmaskArgs& a, int64_t row, int part) {
   const int tid = threadIdx.x;
   const int64_t v0 = (int64_t)part * a.slice;
   const int64_t v1 = min(v0 + a.slice, (int64_t)a.vocab);
@@ -147,9 +153,9 @@ __global__ __launch_bounds__(256) void vocab_reduce_kernel(UnmaskArgs a) {
   }
 }
 
-__global__ __launch_bounds__(64) void commit_kernel(UnmaskArgs a) {
-  const int b = blockIdx.x;
-  const int s = threadIdx.x;
+// Commit rule of sequence b, executed by one full wave (lane = block position).
+__device__ void commit_sequence(const UnmaskArgs& a, int b) {
+  const int s = threadIdx.x & 63;
   const bool in = s < a.S;
   const int64_t r = (int64_t)b * a.S + s;
   const bool masked = in && a.mask[r] != 0;
@@ -195,6 +201,8 @@ __global__ __launch_bounds__(64) void commit_kernel(UnmaskArgs a) {
     if (a.active_next) a.active_next[b] = (any_masked & ~passed) != 0 ? 1 : 0;
   }
 }
+
+__global__ __launch_bounds__(64) void commit_kernel(UnmaskArgs a) { commit_sequence(a, blockIdx.x); }
 
 __global__ __launch_bounds__(64) void loop_init_kernel(const uint8_t* mask, int S, uint8_t* active,
                                                        int32_t* steps_used) {
