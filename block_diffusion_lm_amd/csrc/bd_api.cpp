@@ -43,7 +43,6 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr int kCUs = 256;                  // MI355X compute units
 constexpr size_t kLdsPerCU = 160 * 1024;   // bytes of LDS per compute unit
 constexpr int64_t kMinChunk = 512;         // keys per split below which splitting does not pay
-constexpr int kKeyTile = 64;               // keys per LDS tile of the attention kernel
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -89,11 +88,11 @@ void plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
   const int group = d->n_q_heads / d->n_kv_heads;
   p->head_dim = d->head_dim;
   p->rows = d->block_len * group;
-  // 32 query rows per wave, two waves per SIMD: the hardware interleaves one wave's MFMAs with
-  // the other's softmax. Eight waves share each LDS key tile when the group has > 128 rows.
+  // 32 query rows per wave, two waves per SIMD; eight waves (one workgroup per CU) share each LDS
+  // key tile when the group has more than 128 rows, else four (two workgroups per CU).
   p->rows_per_wave = 32;
   p->waves = p->rows > 128 ? 8 : 4;
-  p->key_tile = kKeyTile;
+  p->key_tile = bd::kAttnKeyTile;
   const int tile_rows = p->waves * p->rows_per_wave;
   p->row_tiles = (p->rows + tile_rows - 1) / tile_rows;
   const int64_t nkeys = d->max_prefix_len + d->block_len;
@@ -103,8 +102,9 @@ void plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
     nsplit = d->num_splits;
   } else {
     // fill every workgroup slot of the chip once, without chunks shorter than kMinChunk keys
-    const size_t lds = 2 * ((size_t)p->key_tile * (d->head_dim * 2 + 16) + (size_t)d->head_dim * p->key_tile * 2);
-    const int by_regs = (p->rows_per_wave == 64 ? 4 : 8) / p->waves;
+    const int row_blocks = p->waves * p->rows_per_wave / 32;
+    const size_t lds = (size_t)bd::attn_stages(d->head_dim, row_blocks) * bd::attn_stage_bytes(d->head_dim);
+    const int by_regs = 8 / row_blocks;   // 512 registers per SIMD lane: 2 waves of 32 rows or 1 of 64
     const int by_lds = (int)(kLdsPerCU / lds);
     const int64_t slots = (int64_t)kCUs * (by_regs < by_lds ? by_regs : by_lds);
     nsplit = (slots + base - 1) / base;

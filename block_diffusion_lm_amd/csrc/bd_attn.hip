@@ -8,9 +8,13 @@
 // Work decomposition. For sequence b and KV head g the R = S * (Hq/Hkv) query rows of the
 // group share one key sequence: the prefix_len[b] cached keys followed by the S block keys.
 // That sequence is cut into chunks; a workgroup owns one (sequence, KV head, chunk, row tile)
-// item. Each wave holds 32*RB query rows in registers (RB 32-row MFMA blocks) and streams the
-// chunk's keys through LDS in tiles of 64 keys, double-buffered, the next tile's global loads
-// in flight while the current one is consumed.
+// item. Each wave holds 32 query rows in registers and streams the chunk's keys through LDS in
+// tiles of 64 keys. Tiles are copied HBM -> LDS by LDS DMA (buffer/global loads with the lds
+// modifier, 16 bytes a lane), so the copy takes no registers and, for tiles inside the cached
+// prefix, no vector ALU work, into a ring of stages several tiles deep; one barrier per tile
+// publishes a landed tile and frees a consumed stage. Within a wave the 32-key blocks are
+// software-pipelined: the QK product of the next block is in flight while the current block's
+// softmax runs.
 //
 // The host plans chunks for the whole batch; when only some sequences are still active (the
 // denoise loop retires sequences as their blocks complete) the kernels re-plan on the device:
@@ -21,15 +25,15 @@
 // S^T = K Q^T (A = 32 keys x 16 dims from LDS, B = Q^T held in registers), so that every lane
 // owns the scores of ONE query row (lane % 32) for 16 of each 32 keys; the other 16 keys of
 // that row sit in lane ^ 32. Row max needs one cross-half swap, row sums none until the end.
-// The output is also accumulated transposed, O^T += V^T P^T (A = V^T from LDS, B = P^T), whose
-// B operand is exactly 8 consecutive accumulator registers of S^T converted to bf16: the key
-// order inside each 16-key step is permuted to match, and V is stored transposed in LDS in the
-// same permuted order, with an XOR swizzle of its 16-byte chunks that keeps both the
-// transposing writes and the operand reads free of bank conflicts.
+// The output is also accumulated transposed, O^T += V^T P^T (A = V^T, B = P^T), whose B operand
+// is exactly 8 consecutive accumulator registers of S^T converted to bf16. V stays row-major in
+// LDS; its A operand is gathered with transposing LDS reads (ds_read_b64_tr_b16) whose per-lane
+// key addresses follow the key order of those accumulator registers. K rows carry one pad chunk
+// and V rows a 64-byte block swizzle, so neither operand read has bank conflicts.
 //
 // Softmax: online (running max m, running sum l) in log2 units, exp2 in float32, P rounded to
 // bf16 for the P V product; l sums the same bf16-rounded P (v_dot2), so numerator and
-// denominator use identical weights. The running max is only raised when a tile's maximum
+// denominator use identical weights. The running max is only raised when a block's maximum
 // exceeds it by more than 8 (log2 units); probabilities relative to a stale max stay below
 // 2^8, which fp32 and bf16 hold exactly as well, so the result is unchanged while rescaling of
 // the output accumulators becomes rare.
@@ -44,11 +48,9 @@ typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyRescale = 8.0f;
-constexpr int kPrioMode = 0;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -108,42 +110,135 @@ __device__ __forceinline__ int rank_active(const uint8_t* active, int b) {
   return r;
 }
 
-template <int D, int KT_>
+template <int D>
 struct Geo {
-  static constexpr int KT = KT_;                    // keys per LDS tile
-  static constexpr int KB = KT / 32;                // 32-key blocks per tile
-  static constexpr int KROW = D * 2 + 16;          // bytes per key row of the K tile (padded)
-  static constexpr int VROW = KT * 2;               // bytes per dim row of the transposed V tile
+  static constexpr int KT = kAttnKeyTile;           // keys per LDS tile
+  static constexpr int KB = KT / 32;                // 32-key MFMA blocks per tile
+  static constexpr int KROW = D * 2 + 16;          // bytes per key row of the K tile: D values + a pad chunk
+  static constexpr int VROW = D * 2;                // bytes per key row of the V tile (64-byte blocks swizzled)
   static constexpr int KBYTES = KT * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int BUF = KBYTES + VBYTES;
-  static constexpr int KS = D / 16;                 // k-steps of Q K^T
+  static constexpr int VBYTES = KT * VROW;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int JK = KBYTES / 1024;          // LDS-DMA wave instructions (64 lanes x 16 B) filling K
+  static constexpr int J = JK + VBYTES / 1024;      // ... filling a whole stage
+  static constexpr int KS = D / 16;                 // k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;                 // 32-dim blocks of the output
+  static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "stage regions must be whole DMA instructions");
+  static_assert(STAGE == attn_stage_bytes(D), "host and device disagree on the stage size");
 };
 
-// Swizzle of the 16-byte chunks of the transposed V tile: chunk c of dim row d is stored at
-// c ^ vt_swz(d). Inside each 16-key step, key 8a+4b+c sits at position 8b+4a+c, so lane half b
-// of the P^T operand reads positions 8b..8b+7 as one 16-byte chunk.
-__device__ __forceinline__ int vt_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
+// 64-byte block swizzle of the V tile: block c of key row k is stored at c ^ vswz(k), so that the
+// four consecutive key rows one transposing read touches lie in four different bank groups.
+template <int D>
+__device__ __forceinline__ int vswz(int k) {
+  return D == 128 ? (k & 3) : ((k >> 1) & 1);
+}
 
-// RB == 1 variants hold half the registers and are meant to run two waves per SIMD.
-template <int D, int NW, int RB, int KT>
-__global__ __launch_bounds__(NW * 64, (RB == 1 && NW < 8) ? 8 / NW : 1) void attn_split_kernel(AttnArgs a) {
-  using G = Geo<D, KT>;
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes, lane r supplies the
+// address of 4 consecutive 16-bit values M[r][0..3]; lane j receives M[(j >> 2) + 4 i][j & 3] for
+// i = 0..3. With lane r pointing at key (r >> 2) and dims 4 (r & 3) .. +3 of a row-major tile, lane
+// j of the group receives dim j of four consecutive keys -- a column of V, i.e. a row of V^T.
+//
+// read_vt gathers the V^T operands of a 32-key block -- two 16-key steps e, every 32-dim block
+// db, two reads each (keys +0..3 and +8..11 of each lane half) -- all issued together and waited
+// for inside the same asm block. (Issued through the compiler, every such read would first wait
+// for all LDS DMA in flight, i.e. for the tiles being prefetched.) addr[db]: LDS byte address of
+// the lane's first key row in block db; OFF: byte offset of the block's first key row.
+template <int D, int OFF>
+__device__ __forceinline__ void read_vt(const uint32_t (&addr)[D / 32], bf16x8 (&vf)[2][D / 32]) {
+  constexpr int R = D * 2;   // bytes per key row
+  static_assert(OFF + 24 * R < 65536, "ds offset range");
+  uint64_t r[2][D / 16];      // [e][2 db + half]
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %2, %17 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %4, %18 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %5, %18 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %6, %19 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %9, %16 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %10, %17 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %11, %17 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %12, %18 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %13, %18 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %14, %19 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]), "=&v"(r[0][4]), "=&v"(r[0][5]),
+          "=&v"(r[0][6]), "=&v"(r[0][7]), "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3]),
+          "=&v"(r[1][4]), "=&v"(r[1][5]), "=&v"(r[1][6]), "=&v"(r[1][7])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(OFF), "i"(OFF + 8 * R), "i"(OFF + 16 * R),
+          "i"(OFF + 24 * R));
+  } else {
+    static_assert(D == 64, "head_dim 64 or 128");
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %2, %9 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %9 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]), "=&v"(r[1][0]), "=&v"(r[1][1]),
+          "=&v"(r[1][2]), "=&v"(r[1][3])
+        : "v"(addr[0]), "v"(addr[1]), "i"(OFF), "i"(OFF + 8 * R), "i"(OFF + 16 * R), "i"(OFF + 24 * R));
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const uint64_t lo = r[e][2 * db], hi = r[e][2 * db + 1];
+      vf[e][db] = __builtin_bit_cast(bf16x8, u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)});
+    }
+}
+
+// LDS DMA of 16 bytes per lane: lane l's 16 bytes at src land at LDS byte dst + 16 l (dst uniform).
+__device__ __forceinline__ void dma16(const char* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// The same through a buffer resource: lane l's 16 bytes at base(rsrc) + soff + voff. The scalar
+// offset carries the tile position, so a tile costs no vector ALU work at all.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (dword 3: the gfx9 raw-buffer format word).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)min(bytes, (uint64_t)0x7fffffff), 0x00020000);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// NW waves of RB 32-row blocks each. NW * RB == 8 (256 rows): one workgroup per CU; NW * RB == 4:
+// two per CU. RB == 2 waves reuse every K and V^T operand read for two MFMAs.
+template <int D, int NW, int RB>
+__global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kernel(AttnArgs a) {
+  using G = Geo<D>;
   constexpr int NT = NW * 64;
-  constexpr int D8 = D / 8;
-  constexpr int ROWS_W = 32 * RB;                    // query rows per wave
-  // keys per loading unit: each thread moves UK rows x 8 dims of K and of V per tile
-  constexpr int UK = ((G::KT / 4) * D8 >= NT) ? 4 : ((G::KT / 2) * D8 >= NT) ? 2 : 1;
-  constexpr int UNITS = (G::KT / UK) * D8;
-  constexpr int UPT = UNITS / NT;
-  static_assert(UPT >= 1 && UNITS % NT == 0, "tile loading does not divide evenly");
+  constexpr int NSTAGE = attn_stages(D, NW * RB);
+  constexpr int JV = G::J - G::JK;
+  constexpr int SK = (G::JK + NW - 1) / NW;       // K / V DMA instructions a wave issues per tile (at most)
+  constexpr int SV = (JV + NW - 1) / NW;
+  constexpr int NMIN = G::JK / NW + JV / NW;       // ... in all (at least): the waits count on this many
+  static_assert(NMIN * 3 < 64 && NSTAGE <= 4, "vmcnt range");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * G::BUF];
+  __shared__ __attribute__((aligned(16))) char smem[NSTAGE * G::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches and bases
   const int lrow = lane & 31;
   const int half = lane >> 5;
 
@@ -151,24 +246,26 @@ __global__ __launch_bounds__(NW * 64, (RB == 1 && NW < 8) ? 8 / NW : 1) void att
   const int64_t nitems = (int64_t)gridDim.x;
   int64_t item = blockIdx.x;
   if ((nitems & 7) == 0) item = (item & 7) * (nitems >> 3) + (item >> 3);
-  const int n_act = count_active(a.active, a.B);
+  // (values loaded from memory are made explicitly wave-uniform, so that the tile bookkeeping
+  // and the DMA bases below live in scalar registers)
+  const int n_act = __builtin_amdgcn_readfirstlane(count_active(a.active, a.B));
   const ItemMap im = device_plan(a, n_act);
   const int rt = (int)(item % a.row_tiles);
   const int64_t ps = item / a.row_tiles;
   const int split = (int)(ps % im.nsplit);
   const int64_t pair_a = ps / im.nsplit;              // pair among the active sequences
   if (pair_a >= (int64_t)n_act * a.Hkv) return;
-  const int b = nth_active(a.active, a.B, (int)(pair_a / a.Hkv));
+  const int b = __builtin_amdgcn_readfirstlane(nth_active(a.active, a.B, (int)(pair_a / a.Hkv)));
   const int g = (int)(pair_a % a.Hkv);
-  const int64_t len = a.prefix_len[b];
+  const int64_t len = __builtin_amdgcn_readfirstlane(a.prefix_len[b]);
   const int64_t nkeys = len + a.S;
   const int64_t k_begin = (int64_t)split * im.chunk;
   if (k_begin >= nkeys) return;
   const int64_t k_end = min(k_begin + im.chunk, nkeys);
   const int ntiles = (int)((k_end - k_begin + G::KT - 1) / G::KT);
 
-  const int tile_rows = NW * ROWS_W;
-  const int row0 = rt * tile_rows + wave * ROWS_W;    // first query row of this wave
+  const int tile_rows = NW * RB * 32;
+  const int row0 = rt * tile_rows + wave * RB * 32;   // first query row of this wave
   const bool wave_rows = row0 < a.rows;
 
   // ---- Q fragments: B operand of S^T = K Q^T (lane: row lrow, dims 8*half .. +7 of a k-step)
@@ -194,81 +291,76 @@ __global__ __launch_bounds__(NW * 64, (RB == 1 && NW < 8) ? 8 / NW : 1) void att
   const uint16_t* kb0 = a.k_blk + ((int64_t)b * a.S * a.Hkv + g) * D;
   const uint16_t* vb0 = a.v_blk + ((int64_t)b * a.S * a.Hkv + g) * D;
 
-  // ---- tile loading: registers hold the next tile while the current one is consumed.
-  // A tile that lies wholly inside the prefix and the chunk (all but at most two per chunk)
-  // is one uniform base pointer plus per-thread constant offsets.
-  u32x4 kreg[UK], vreg[UK];
-  auto load_unit = [&](int64_t kt0, int i) {
-    const int u = tid + NT * i;
-    const int d8 = (u % D8) * 8;
-    const int kk = (u / D8) * UK;
+  // ---- tile filling by LDS DMA. A stage is JK + JV wave instructions of 1 KB (64 lanes x 16 B):
+  // K instruction j writes stage bytes [1024 j, 1024 j + 1024), V instruction j the same range of
+  // the V region; wave w issues instructions w, w + NW, ... of each. koff / voff: byte offset,
+  // from the tile's first key row, of the 16 source bytes this lane moves in each of its
+  // instructions -- K rows are copied with a pad chunk (a copy of the row's last chunk), V rows
+  // with their 64-byte blocks swizzled.
+  // buffer resources over this (sequence, KV head)'s cached rows (buffer offsets are 32-bit)
+  const __amdgpu_buffer_rsrc_t rsrc_k = raw_rsrc(kc, (uint64_t)a.lcap * D * 2);
+  const __amdgpu_buffer_rsrc_t rsrc_v = raw_rsrc(vc, (uint64_t)a.lcap * D * 2);
+  uint32_t koff[SK], voff[SV];
+#pragma unroll
+  for (int i = 0; i < SK; ++i) {
+    const int p = (wave + NW * i) * 1024 + lane * 16;
+    const int row = p / G::KROW;
+    const int ch = min((p % G::KROW) / 16, D / 8 - 1);
+    koff[i] = (uint32_t)(row * D * 2 + ch * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < SV; ++i) {
+    const int p = (wave + NW * i) * 1024 + lane * 16;
+    const int row = p / G::VROW;
+    const int blk = (p % G::VROW) / 64;
+    voff[i] = (uint32_t)(row * G::VROW + ((blk ^ vswz<D>(row)) * 64) + (p % 64));
+  }
+  // The tile at kt0 into stage `stage`. A tile that lies wholly inside the cached prefix and the
+  // chunk (all but at most two per chunk) is one uniform base per tensor; otherwise sources are
+  // per lane: cache rows, block rows past the prefix end, and rows past the chunk end repeating
+  // its last key (finite data whose scores are masked).
+  auto issue_tile = [&](int stage, int64_t kt0) {
+    char* dst = smem + stage * G::STAGE;
     if (kt0 + G::KT <= len && kt0 + G::KT <= k_end) {
-      const uint16_t* kp = kc + kt0 * D + kk * D + d8;
-      const uint16_t* vp = vc + kt0 * D + kk * D + d8;
+      const uint32_t soff = (uint32_t)(kt0 * D * 2);
 #pragma unroll
-      for (int j = 0; j < UK; ++j) {
-        kreg[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + j * D));
-        vreg[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + j * D));
-      }
+      for (int i = 0; i < SK; ++i)
+        if (wave + NW * i < G::JK) dma16_buf(rsrc_k, koff[i], soff, dst + (wave + NW * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < SV; ++i)
+        if (wave + NW * i < JV) dma16_buf(rsrc_v, voff[i], soff, dst + G::KBYTES + (wave + NW * i) * 1024);
     } else {
+      auto src_of = [&](uint32_t off, const uint16_t* cache, const uint16_t* blk) {
+        const int64_t key = min(kt0 + (int64_t)(off / (D * 2)), k_end - 1);
+        const uint16_t* row = key < len ? cache + key * D : blk + (key - len) * blk_stride;
+        return reinterpret_cast<const char*>(row) + off % (D * 2);
+      };
 #pragma unroll
-      for (int j = 0; j < UK; ++j) {
-        const int64_t key = kt0 + kk + j;
-        if (key < k_end) {
-          const uint16_t* kp = key < len ? kc + key * D : kb0 + (key - len) * blk_stride;
-          const uint16_t* vp = key < len ? vc + key * D : vb0 + (key - len) * blk_stride;
-          kreg[j] = ldg16(kp + d8);
-          vreg[j] = ldg16(vp + d8);
-        } else {
-          kreg[j] = u32x4{0, 0, 0, 0};
-          vreg[j] = u32x4{0, 0, 0, 0};
-        }
-      }
-    }
-  };
-  auto store_unit = [&](char* buf, int i) {
-    char* ks = buf;
-    char* vt = buf + G::KBYTES;
-    const int u = tid + NT * i;
-    const int d8 = (u % D8) * 8;
-    const int kk = (u / D8) * UK;
+      for (int i = 0; i < SK; ++i)
+        if (wave + NW * i < G::JK) dma16(src_of(koff[i], kc, kb0), dst + (wave + NW * i) * 1024);
 #pragma unroll
-    for (int j = 0; j < UK; ++j) *reinterpret_cast<u32x4*>(ks + (kk + j) * G::KROW + d8 * 2) = kreg[j];
-    // transposed V: dim rows d8 .. d8+7, keys kk .. kk+UK-1 (consecutive positions)
-    const int k16 = kk & 15;
-    const int a8 = k16 >> 3, b4 = (k16 >> 2) & 1, c = k16 & 3;
-    const int chunk = ((kk >> 4) << 1) + b4;              // 16-byte chunk of the position
-    const int inchunk = (a8 * 4 + c) * 2;                 // byte offset inside that chunk
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-#pragma unroll
-      for (int hi = 0; hi < 2; ++hi) {
-        const int d = d8 + 2 * w + hi;
-        char* dst = vt + d * G::VROW + ((chunk ^ vt_swz(d)) << 4) + inchunk;
-        if constexpr (UK == 4) {
-          const uint32_t x0 = vreg[0][w], x1 = vreg[1][w], x2 = vreg[2][w], x3 = vreg[3][w];
-          u32x2 v;
-          if (hi == 0) {
-            v[0] = (x0 & 0xffffu) | (x1 << 16);
-            v[1] = (x2 & 0xffffu) | (x3 << 16);
-          } else {
-            v[0] = (x0 >> 16) | (x1 & 0xffff0000u);
-            v[1] = (x2 >> 16) | (x3 & 0xffff0000u);
-          }
-          *reinterpret_cast<u32x2*>(dst) = v;
-        } else if constexpr (UK == 2) {
-          const uint32_t x0 = vreg[0][w], x1 = vreg[1][w];
-          *reinterpret_cast<uint32_t*>(dst) = hi == 0 ? ((x0 & 0xffffu) | (x1 << 16)) : ((x0 >> 16) | (x1 & 0xffff0000u));
-        } else {
-          const uint32_t x0 = vreg[0][w];
-          *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(hi == 0 ? (x0 & 0xffffu) : (x0 >> 16));
-        }
-      }
+      for (int i = 0; i < SV; ++i)
+        if (wave + NW * i < JV) dma16(src_of(voff[i], vc, vb0), dst + G::KBYTES + (wave + NW * i) * 1024);
     }
   };
 
-  float m_run[RB], l_run[RB];        // running max (log2 units) and this lane's share of the sum
-  f32x16 o[G::DB][RB];
+  // ---- operand addresses inside a stage
+  // K fragment (A of S^T = K Q^T): key kb*32 + lrow, dims 16 kstep + 8 half .. +7
+  const uint32_t k_lane = (uint32_t)(lrow * G::KROW + half * 16);
+  // V^T fragment (A of O^T = V^T P^T) for 32-dim block db: two transposing reads, keys
+  // 16e + 4 half + 0..3 and 16e + 8 + 4 half + 0..3 -- the key order of the P^T operand below.
+  uint32_t v_lane[G::DB];
+  {
+    const int r = lane & 15;
+    const int key = 4 * half + (r >> 2);
+    const int dpart = 32 * ((lane >> 4) & 1) + 8 * (r & 3);   // bytes inside the 64-byte block
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) v_lane[db] = (uint32_t)(key * G::VROW + ((db ^ vswz<D>(key)) * 64) + dpart);
+  }
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+
+  float m_run[RB], l_run[RB];   // running max (log2 units) and this lane's share of the sum
+  f32x16 o[RB][G::DB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m_run[rb] = -INFINITY;
@@ -276,113 +368,171 @@ __global__ __launch_bounds__(NW * 64, (RB == 1 && NW < 8) ? 8 / NW : 1) void att
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][rb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) o[rb][db][r] = 0.f;
   }
   const float sc = a.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  if constexpr (kPrioMode == 1) {
-    if (wave >= NW / 2) __builtin_amdgcn_s_setprio(1);
-  }
 
-  // With few threads per workgroup a tile is too many registers to hold in flight: those
-  // variants load and store a tile right before consuming it.
-  constexpr bool kPrefetch = UPT <= 1;
-  if (kPrefetch) load_unit(k_begin, 0);
-  for (int t = 0; t < ntiles; ++t) {
-    char* buf = smem + (t & 1) * G::BUF;
-    const int64_t kt0 = k_begin + (int64_t)t * G::KT;
-    if (kPrefetch) {
-      store_unit(buf, 0);
-    } else {
-      for (int i = 0; i < UPT; ++i) {
-        load_unit(kt0, i);
-        store_unit(buf, i);
-      }
+  // this wave's DMA of a tile has landed once at most NMIN * (tiles issued after it) remain;
+  // after the barrier every wave's has
+  auto wait_tile = [&](int pending) {
+    asm volatile("" ::: "memory");
+    if (pending >= 3) wait_vm_lds<NMIN * 3>();
+    else if (pending == 2) wait_vm_lds<NMIN * 2>();
+    else if (pending == 1) wait_vm_lds<NMIN>();
+    else wait_vm_lds<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // K fragments of block kb of the tile in stage st, and S^T = K Q^T from them
+  auto load_k = [&](int st, int kb, bf16x8 (&kf)[G::KS]) {
+    const char* ks = smem + st * G::STAGE + k_lane + kb * 32 * G::KROW;
+#pragma unroll
+    for (int kstep = 0; kstep < G::KS; ++kstep) kf[kstep] = *reinterpret_cast<const bf16x8*>(ks + kstep * 32);
+  };
+  auto qk = [&](const bf16x8 (&kf)[G::KS], f32x16 (&sacc)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
+#pragma unroll
+    for (int kstep = 0; kstep < G::KS; ++kstep)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sacc[rb] = mfma32(kf[kstep], qf[rb][kstep], sacc[rb]);
+  };
+  // keys past the chunk end do not exist for this item (a block with `keys` < 32 existing keys)
+  auto mask_tail = [&](f32x16 (&sacc)[RB], int keys) {
+    if (keys < 32) {
+      const int lim = keys - 4 * half;   // register r holds key 8 (r / 4) + 4 half + r % 4
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) >= lim)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) sacc[rb][r] = -INFINITY;
     }
-    __syncthreads();
-    if (kPrefetch && t + 1 < ntiles) load_unit(kt0 + G::KT, 0);
-    if (!wave_rows) continue;
-
-    const char* ks = buf;
-    const char* vt = buf + G::KBYTES;
-    const int valid = (int)min((int64_t)G::KT, k_end - kt0);   // keys of this tile inside the chunk
-
+  };
+  // block row maxima in log2 units
+  auto row_max = [&](const f32x16 (&sacc)[RB], float (&mx)[RB]) {
 #pragma unroll
-    for (int kb = 0; kb < G::KB; ++kb) {
-      if (kb * 32 >= valid) break;
-      // ---- S^T = K Q^T for 32 keys: sacc[rb], 32 keys x 32 rows each
-      if constexpr (kPrioMode == 2) __builtin_amdgcn_s_setprio(1);
-      f32x16 sacc[RB];
+    for (int rb = 0; rb < RB; ++rb) {
+      float v = sacc[rb][0];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int r = 1; r < 16; ++r) v = fmaxf(v, sacc[rb][r]);
+      mx[rb] = fmaxf(v, other_half(v)) * sc;
+    }
+  };
+  // lazy rescale: raise the running max only when the block's exceeds it by more than
+  // kLazyRescale (rare after the first block)
+  auto rescale = [&](const float (&mx)[RB], bool live) {
+    bool raise_any = false;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
-#pragma unroll
-      for (int kstep = 0; kstep < G::KS; ++kstep) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + lrow) * G::KROW + (kstep * 16 + 8 * half) * 2);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sacc[rb] = mfma32(kf, qf[rb][kstep], sacc[rb]);
-      }
-      if (kb * 32 + 32 > valid) {   // keys past the chunk end do not exist for this item
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= valid)
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) sacc[rb][r] = -INFINITY;
-        }
-      }
-      if constexpr (kPrioMode == 2) __builtin_amdgcn_s_setprio(0);
-      // ---- running max: one (rarely taken) rescale branch per 32 keys
-      float mx[RB];
-      bool raise_any = false;
+    for (int rb = 0; rb < RB; ++rb) raise_any |= live && mx[rb] > m_run[rb] + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(raise_any)) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        float v = sacc[rb][0];
+        const float mnew = live && mx[rb] > m_run[rb] + kLazyRescale ? mx[rb] : m_run[rb];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - mnew);   // exp2(-inf) = 0
+        l_run[rb] *= alpha;
 #pragma unroll
-        for (int r = 1; r < 16; ++r) v = fmaxf(v, sacc[rb][r]);
-        mx[rb] = fmaxf(v, other_half(v)) * sc;
-        raise_any |= mx[rb] > m_run[rb] + kLazyRescale;
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
+        m_run[rb] = mnew;
       }
-      if (__builtin_amdgcn_ballot_w64(raise_any)) {
+    }
+  };
+  // P = exp2(s*sc - m) in bf16, row sums of the rounded P, O^T += V^T P^T
+  auto exp_pv = [&](const f32x16 (&sacc)[RB], const bf16x8 (&vf)[2][G::DB]) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const float mnew = mx[rb] > m_run[rb] + kLazyRescale ? mx[rb] : m_run[rb];
-          const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - mnew);   // exp2(-inf) = 0
-          l_run[rb] *= alpha;
+    for (int e = 0; e < 2; ++e) {
+      bf16x8 pf[RB];
 #pragma unroll
-          for (int db = 0; db < G::DB; ++db)
+      for (int rb = 0; rb < RB; ++rb) {
+        const float mneg = -m_run[rb];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][rb][r] *= alpha;
-          m_run[rb] = mnew;
+        for (int i = 0; i < 8; ++i) pf[rb][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[rb][8 * e + i], sc, mneg));
+        float ls = l_run[rb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2 p2 = {pf[rb][2 * i], pf[rb][2 * i + 1]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, ls, false);
         }
+        l_run[rb] = ls;
       }
-      // ---- P = exp2(s*sc - m) in bf16, row sums of the rounded P, O^T += V^T P^T
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        bf16x8 pf[RB];
+      for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const float mneg = -m_run[rb];
+        for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma32(vf[e][db], pf[rb], o[rb][db]);
+    }
+  };
+
+  // ---- software pipeline over 32-key blocks. Each block reads the K fragments of the next block
+  // first, then its own V^T operands (one LDS round trip for both), and issues the next block's
+  // QK product in the same straight-line region as its own row maxima, and its exponentials in
+  // the same region as its P V products, so one wave's MFMAs and VALU work can overlap. A QK
+  // product of a block that does not exist (past the last tile, or the odd half of a short last
+  // tile) reads stale but in-bounds LDS and is never used.
+  //
+  // Ring of NSTAGE >= 3 stages: tile t + 1 is published by a barrier between the two blocks of
+  // tile t, which also frees tile t - 1's stage for tile t + NSTAGE - 1 (NSTAGE - 2 tiles of DMA
+  // stay in flight). With 2 stages, tile t + 1 is published after tile t's odd block has read its
+  // V^T operands, freeing tile t's stage for tile t + 2.
+  static_assert(G::KB == 2, "two 32-key blocks per tile");
+  constexpr int AHEAD = NSTAGE >= 3 ? NSTAGE - 1 : NSTAGE;   // tiles issued before the loop
 #pragma unroll
-          for (int i = 0; i < 8; ++i) pf[rb][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[rb][8 * e + i], sc, mneg));
-          float ls = l_run[rb];
+  for (int s = 0; s < AHEAD; ++s)
+    if (s < ntiles) issue_tile(s, k_begin + (int64_t)s * G::KT);
+  wait_tile(min(AHEAD - 1, ntiles - 1));
+  f32x16 s_even[RB], s_odd[RB];   // S^T of the even and the odd block of a tile
+  if (wave_rows) {
+    bf16x8 kf[G::KS];
+    load_k(0, 0, kf);
+    qk(kf, s_even);
+  }
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t % NSTAGE;
+    const int valid = (int)min((int64_t)G::KT, k_end - (k_begin + (int64_t)t * G::KT));   // keys of tile t
+    const bool odd = valid > 32;                  // tile t has a second block
+    uint32_t vaddr[G::DB];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bf16x2 p2 = {pf[rb][2 * i], pf[rb][2 * i + 1]};
-            ls = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, ls, false);
-          }
-          l_run[rb] = ls;
-        }
-        const int chunk = (kb * 2 + e) * 2 + half;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db) {
-          const int d = db * 32 + lrow;
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + d * G::VROW + ((chunk ^ vt_swz(d)) << 4));
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) o[db][rb] = mfma32(vf, pf[rb], o[db][rb]);
-        }
+    for (int db = 0; db < G::DB; ++db) vaddr[db] = smem_lds + st * G::STAGE + G::KBYTES + v_lane[db];
+    bf16x8 vf[2][G::DB];
+    float mx[RB];
+    // ---- even block
+    if (wave_rows) {
+      bf16x8 kf[G::KS];
+      load_k(st, 1, kf);
+      read_vt<D, 0>(vaddr, vf);
+      mask_tail(s_even, min(valid, 32));
+      qk(kf, s_odd);
+      row_max(s_even, mx);
+      rescale(mx, true);
+      exp_pv(s_even, vf);
+    }
+    if constexpr (NSTAGE >= 3) {
+      // publish tile t + 1; tile t - 1's stage is free (waves without rows take part too)
+      wait_tile(min(NSTAGE - 3, ntiles - 2 - t));
+      if (t + NSTAGE - 1 < ntiles) issue_tile((t + NSTAGE - 1) % NSTAGE, k_begin + (int64_t)(t + NSTAGE - 1) * G::KT);
+    }
+    // ---- odd block
+    if (wave_rows) {
+      bf16x8 kf[G::KS];
+      if constexpr (NSTAGE >= 3) load_k((t + 1) % NSTAGE, 0, kf);
+      read_vt<D, 32 * G::VROW>(vaddr, vf);
+      mask_tail(s_odd, max(valid - 32, 0));
+      if constexpr (NSTAGE < 3) {
+        wait_tile(min(NSTAGE - 2, ntiles - 2 - t));
+        if (t + NSTAGE < ntiles) issue_tile(st, k_begin + (int64_t)(t + NSTAGE) * G::KT);
+        load_k((t + 1) % NSTAGE, 0, kf);
       }
+      qk(kf, s_even);
+      row_max(s_odd, mx);
+      rescale(mx, odd);
+      if (odd) exp_pv(s_odd, vf);
+    } else if constexpr (NSTAGE < 3) {
+      wait_tile(min(NSTAGE - 2, ntiles - 2 - t));
+      if (t + NSTAGE < ntiles) issue_tile(st, k_begin + (int64_t)(t + NSTAGE) * G::KT);
     }
   }
   if (!wave_rows) return;
@@ -406,7 +556,7 @@ __global__ __launch_bounds__(NW * 64, (RB == 1 && NW < 8) ? 8 / NW : 1) void att
           const int d = db * 32 + 8 * q4 + 4 * half;
           bf16x4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[db][rb][4 * q4 + i] * inv);
+          for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[rb][db][4 * q4 + i] * inv);
           *reinterpret_cast<bf16x4*>(op + d) = v;
         }
       if (a.lse && half == 0) a.lse[((int64_t)b * a.Hq + hq) * a.S + s] = (m_run[rb] + log2f(l_tot)) * kLn2;
@@ -419,7 +569,7 @@ __global__ __launch_bounds__(NW * 64, (RB == 1 && NW < 8) ? 8 / NW : 1) void att
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int d = db * 32 + 8 * q4 + 4 * half;
-          const f32x4 v = {o[db][rb][4 * q4], o[db][rb][4 * q4 + 1], o[db][rb][4 * q4 + 2], o[db][rb][4 * q4 + 3]};
+          const f32x4 v = {o[rb][db][4 * q4], o[rb][db][4 * q4 + 1], o[rb][db][4 * q4 + 2], o[rb][db][4 * q4 + 3]};
           *reinterpret_cast<f32x4*>(ap + d) = v;
         }
       if (half == 0) {
@@ -428,6 +578,7 @@ __global__ __launch_bounds__(NW * 64, (RB == 1 && NW < 8) ? 8 / NW : 1) void att
       }
     }
   }
+  (void)NT;
 }
 
 // Merge of the chunk partials of every (sequence, KV head, query row): with M = max_c m_c,
@@ -562,33 +713,21 @@ __global__ __launch_bounds__(256) void attn_merge_wide_kernel(AttnArgs a, int ti
   if (a.lse && dg == 0) a.lse[((int64_t)b * a.Hq + hq) * a.S + s] = (M + log2f(den)) * kLn2;
 }
 
-template <int D, int NW, int RB>
-hipError_t launch_split_t(const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
-  if (plan.key_tile == 128)
-    hipLaunchKernelGGL((attn_split_kernel<D, NW, RB, 128>), dim3((unsigned)plan.n_items), dim3(NW * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_split_kernel<D, NW, RB, 64>), dim3((unsigned)plan.n_items), dim3(NW * 64), 0, stream, a);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_attn_split(const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
-  const int key = plan.waves * 100 + plan.rows_per_wave;
-  if (plan.head_dim == 128) {
-    switch (key) {
-      case 464: return launch_split_t<128, 4, 2>(plan, a, stream);
-      case 432: return launch_split_t<128, 4, 1>(plan, a, stream);
-      case 832: return launch_split_t<128, 8, 1>(plan, a, stream);
-    }
-  } else if (plan.head_dim == 64) {
-    switch (key) {
-      case 464: return launch_split_t<64, 4, 2>(plan, a, stream);
-      case 432: return launch_split_t<64, 4, 1>(plan, a, stream);
-      case 832: return launch_split_t<64, 8, 1>(plan, a, stream);
-    }
+  if (plan.key_tile != kAttnKeyTile) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)plan.n_items);
+  const dim3 block((unsigned)plan.waves * 64);
+  const int key = plan.head_dim * 1000 + plan.waves * 100 + plan.rows_per_wave;
+  switch (key) {
+    case 128832: hipLaunchKernelGGL((attn_split_kernel<128, 8, 1>), grid, block, 0, stream, a); break;
+    case 128432: hipLaunchKernelGGL((attn_split_kernel<128, 4, 1>), grid, block, 0, stream, a); break;
+    case 64832: hipLaunchKernelGGL((attn_split_kernel<64, 8, 1>), grid, block, 0, stream, a); break;
+    case 64432: hipLaunchKernelGGL((attn_split_kernel<64, 4, 1>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_merge(const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {

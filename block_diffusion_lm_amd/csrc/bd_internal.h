@@ -12,13 +12,21 @@ namespace bd {
 // attention
 // ---------------------------------------------------------------------------------------------
 
+// LDS ring of the attention split kernel, shared by the kernel and the host planner: a stage holds
+// one tile of kAttnKeyTile keys (K rows with one 16-byte pad chunk each, then unpadded V rows).
+constexpr int kAttnKeyTile = 64;
+constexpr int attn_stage_bytes(int head_dim) { return kAttnKeyTile * (head_dim * 2 + 16) + kAttnKeyTile * head_dim * 2; }
+// stages in the ring: 256-row workgroups (one per CU) prefetch three tiles ahead; 128-row
+// workgroups (two per CU) one, except at head_dim 64 where four stages still fit twice.
+constexpr int attn_stages(int head_dim, int row_blocks) { return (row_blocks == 8 || head_dim == 64) ? 4 : 2; }
+
 struct AttnPlan {
   int head_dim;       // D
-  int waves;          // waves per workgroup (1, 2, 4 or 8)
+  int waves;          // waves per workgroup (4 or 8)
   int rows_per_wave;  // 32 or 64 (one or two 32-row MFMA blocks); a workgroup owns waves*rows_per_wave rows
   int rows;           // R = S * (Hq / Hkv): query rows per (sequence, KV head)
   int row_tiles;      // ceil(R / (waves * rows_per_wave))
-  int key_tile;       // keys staged through LDS per iteration (64 or 128)
+  int key_tile;       // keys staged through LDS per iteration (kAttnKeyTile)
   int64_t chunk;      // keys per split (multiple of 64)
   int nsplit;         // splits per (sequence, KV head)
   int64_t n_items;    // B * Hkv * nsplit * row_tiles workgroups
