@@ -46,19 +46,22 @@ constexpr int64_t kMinChunk = 512;         // keys per split below which splitti
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Launch wrapper: brackets the launch with trace events when a trace is attached.
+// Launch wrapper: when a trace is attached, the kernel's dispatch stamps the record's events.
 template <typename F>
 bd_status traced(const char* name, hipStream_t stream, F&& launch) {
   bd_trace* tr = g_trace;
-  bd_trace::Rec* rec = nullptr;
+  bd::Launch l{stream};
   if (tr && tr->count < (int32_t)tr->recs.size()) {
-    rec = &tr->recs[tr->count++];
+    bd_trace::Rec* rec = &tr->recs[tr->count++];
     rec->name = name;
-    if (hipEventRecord(rec->start, stream) != hipSuccess) return fail(BD_EHIP, "hipEventRecord failed");
+    l.start = rec->start;
+    l.stop = rec->stop;
+    // let the stream drain first: the start stamp is taken when the dispatch is processed, which
+    // would otherwise include the wait for the previous kernel
+    if (hipStreamSynchronize(stream) != hipSuccess) return fail(BD_EHIP, "hipStreamSynchronize failed");
   }
-  hipError_t e = launch();
+  hipError_t e = launch(l);
   if (e != hipSuccess) return fail(BD_EHIP, "launch of %s failed: %s", name, hipGetErrorString(e));
-  if (rec && hipEventRecord(rec->stop, stream) != hipSuccess) return fail(BD_EHIP, "hipEventRecord failed");
   return BD_OK;
 }
 
@@ -176,9 +179,9 @@ bd_status run_attn(const bd_attn_desc* d, const bd::AttnPlan& plan, const void* 
   const float tau = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
   a.scale_log2 = tau * 1.4426950408889634f;
   a.direct = plan.direct ? 1 : 0;
-  bd_status st = traced("attn_split", stream, [&] { return bd::launch_attn_split(plan, a, stream); });
+  bd_status st = traced("attn_split", stream, [&](const bd::Launch& l) { return bd::launch_attn_split(plan, a, l); });
   if (st != BD_OK || plan.direct) return st;
-  return traced("attn_merge", stream, [&] { return bd::launch_attn_merge(plan, a, stream); });
+  return traced("attn_merge", stream, [&](const bd::Launch& l) { return bd::launch_attn_merge(plan, a, l); });
 }
 
 // ------------------------------------------------------------------------------------------
@@ -250,9 +253,9 @@ bd_status run_unmask(const bd_unmask_desc* d, const bd::UnmaskPlan& plan, const 
   a.step = step;
   a.steps_used = steps_used;
   a.active_next = active_next;
-  bd_status st = traced("vocab_reduce", stream, [&] { return bd::launch_vocab_reduce(a, stream); });
+  bd_status st = traced("vocab_reduce", stream, [&](const bd::Launch& l) { return bd::launch_vocab_reduce(a, l); });
   if (st != BD_OK) return st;
-  return traced("commit", stream, [&] { return bd::launch_commit(a, stream); });
+  return traced("commit", stream, [&](const bd::Launch& l) { return bd::launch_commit(a, l); });
 }
 
 // denoise-loop workspace: [attention partials][unmask partials][active flags]
@@ -361,7 +364,7 @@ bd_status bd_denoise_block(const bd_attn_desc* attn, const bd_unmask_desc* unmas
   uint8_t* active = reinterpret_cast<uint8_t*>(w + ap.bytes + up.bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  st = traced("loop_init", s, [&] { return bd::launch_loop_init(mask, attn->batch, attn->block_len, active, steps_used, s); });
+  st = traced("loop_init", s, [&](const bd::Launch& l) { return bd::launch_loop_init(mask, attn->batch, attn->block_len, active, steps_used, l); });
   if (st != BD_OK) return st;
   for (int32_t t = t0; t < T; ++t) {
     const void *q = nullptr, *kb = nullptr, *vb = nullptr;

@@ -715,38 +715,32 @@ __global__ __launch_bounds__(256) void attn_merge_wide_kernel(AttnArgs a, int ti
 
 }  // namespace
 
-hipError_t launch_attn_split(const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_attn_split(const AttnPlan& plan, const AttnArgs& a, const Launch& l) {
   if (plan.key_tile != kAttnKeyTile) return hipErrorInvalidValue;
   const dim3 grid((unsigned)plan.n_items);
   const dim3 block((unsigned)plan.waves * 64);
   const int key = plan.head_dim * 1000 + plan.waves * 100 + plan.rows_per_wave;
   switch (key) {
-    case 128832: hipLaunchKernelGGL((attn_split_kernel<128, 8, 1>), grid, block, 0, stream, a); break;
-    case 128432: hipLaunchKernelGGL((attn_split_kernel<128, 4, 1>), grid, block, 0, stream, a); break;
-    case 64832: hipLaunchKernelGGL((attn_split_kernel<64, 8, 1>), grid, block, 0, stream, a); break;
-    case 64432: hipLaunchKernelGGL((attn_split_kernel<64, 4, 1>), grid, block, 0, stream, a); break;
+    case 128832: return launch_kernel(attn_split_kernel<128, 8, 1>, grid, block, l, a);
+    case 128432: return launch_kernel(attn_split_kernel<128, 4, 1>, grid, block, l, a);
+    case 64832: return launch_kernel(attn_split_kernel<64, 8, 1>, grid, block, l, a);
+    case 64432: return launch_kernel(attn_split_kernel<64, 4, 1>, grid, block, l, a);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
-hipError_t launch_attn_merge(const AttnPlan& plan, const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_attn_merge(const AttnPlan& plan, const AttnArgs& a, const Launch& l) {
   const int64_t rows = (int64_t)a.B * a.Hkv * a.rows;
   const int tile_rows = plan.waves * plan.rows_per_wave;
   if (plan.head_dim != 128 && plan.head_dim != 64) return hipErrorInvalidValue;
   if (plan.wide_merge) {
-    if (plan.head_dim == 128)
-      hipLaunchKernelGGL((attn_merge_wide_kernel<128>), dim3((unsigned)rows), dim3(256), 0, stream, a, tile_rows);
-    else
-      hipLaunchKernelGGL((attn_merge_wide_kernel<64>), dim3((unsigned)rows), dim3(256), 0, stream, a, tile_rows);
-  } else {
-    const unsigned blocks = (unsigned)((rows * (plan.head_dim / 4) + 255) / 256);
-    if (plan.head_dim == 128)
-      hipLaunchKernelGGL((attn_merge_narrow_kernel<128>), dim3(blocks), dim3(256), 0, stream, a, tile_rows);
-    else
-      hipLaunchKernelGGL((attn_merge_narrow_kernel<64>), dim3(blocks), dim3(256), 0, stream, a, tile_rows);
+    const dim3 grid((unsigned)rows);
+    return plan.head_dim == 128 ? launch_kernel(attn_merge_wide_kernel<128>, grid, dim3(256), l, a, tile_rows)
+                                : launch_kernel(attn_merge_wide_kernel<64>, grid, dim3(256), l, a, tile_rows);
   }
-  return hipGetLastError();
+  const dim3 grid((unsigned)((rows * (plan.head_dim / 4) + 255) / 256));
+  return plan.head_dim == 128 ? launch_kernel(attn_merge_narrow_kernel<128>, grid, dim3(256), l, a, tile_rows)
+                              : launch_kernel(attn_merge_narrow_kernel<64>, grid, dim3(256), l, a, tile_rows);
 }
 
 }  // namespace bd

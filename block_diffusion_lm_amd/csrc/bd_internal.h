@@ -2,11 +2,26 @@
 // (bd_attn.hip, bd_unmask.hip). Not installed; the public ABI is include/bd.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace bd {
+
+// Where a kernel goes: its stream and, when a trace is attached, the events that the dispatch
+// itself stamps at kernel start and end (hipExtLaunchKernelGGL), so a traced duration is the
+// kernel's own, without the gaps of separately recorded events.
+struct Launch {
+  hipStream_t stream;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename K, typename... Args>
+hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, const Launch& l, Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, l.stream, l.start, l.stop, 0, args...);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------------------------
 // attention
@@ -56,8 +71,8 @@ struct AttnArgs {
   int direct;
 };
 
-hipError_t launch_attn_split(const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
-hipError_t launch_attn_merge(const AttnPlan& plan, const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_split(const AttnPlan& plan, const AttnArgs& a, const Launch& l);
+hipError_t launch_attn_merge(const AttnPlan& plan, const AttnArgs& a, const Launch& l);
 
 // ---------------------------------------------------------------------------------------------
 // confidence unmasking
@@ -90,9 +105,8 @@ struct UnmaskArgs {
   uint8_t* active_next;         // [B]: whether a masked position remains after the commit
 };
 
-hipError_t launch_vocab_reduce(const UnmaskArgs& a, hipStream_t stream);
-hipError_t launch_commit(const UnmaskArgs& a, hipStream_t stream);
-hipError_t launch_loop_init(const uint8_t* mask, int B, int S, uint8_t* active, int32_t* steps_used,
-                            hipStream_t stream);
+hipError_t launch_vocab_reduce(const UnmaskArgs& a, const Launch& l);
+hipError_t launch_commit(const UnmaskArgs& a, const Launch& l);
+hipError_t launch_loop_init(const uint8_t* mask, int B, int S, uint8_t* active, int32_t* steps_used, const Launch& l);
 
 }  // namespace bd

@@ -218,21 +218,17 @@ __global__ __launch_bounds__(64) void loop_init_kernel(const uint8_t* mask, int 
 
 }  // namespace
 
-hipError_t launch_vocab_reduce(const UnmaskArgs& a, hipStream_t stream) {
+hipError_t launch_vocab_reduce(const UnmaskArgs& a, const Launch& l) {
   const int64_t blocks = (int64_t)a.B * a.S * a.vsplit;
-  hipLaunchKernelGGL(vocab_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(vocab_reduce_kernel, dim3((unsigned)blocks), dim3(256), l, a);
 }
 
-hipError_t launch_commit(const UnmaskArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(commit_kernel, dim3((unsigned)a.B), dim3(64), 0, stream, a);
-  return hipGetLastError();
+hipError_t launch_commit(const UnmaskArgs& a, const Launch& l) {
+  return launch_kernel(commit_kernel, dim3((unsigned)a.B), dim3(64), l, a);
 }
 
-hipError_t launch_loop_init(const uint8_t* mask, int B, int S, uint8_t* active, int32_t* steps_used,
-                            hipStream_t stream) {
-  hipLaunchKernelGGL(loop_init_kernel, dim3((unsigned)B), dim3(64), 0, stream, mask, S, active, steps_used);
-  return hipGetLastError();
+hipError_t launch_loop_init(const uint8_t* mask, int B, int S, uint8_t* active, int32_t* steps_used, const Launch& l) {
+  return launch_kernel(loop_init_kernel, dim3((unsigned)B), dim3(64), l, mask, S, active, steps_used);
 }
 
 }  // namespace bd

@@ -199,8 +199,11 @@ const char* bd_last_error(void);
  * Kernel tracing (observability; off unless a trace is attached)
  *
  * While a trace is attached to the calling thread, every kernel the library enqueues from that
- * thread is bracketed by two HIP events recorded on the launch stream. bd_trace_get waits for
- * the events of record i and returns the kernel name and its duration.
+ * thread carries two HIP events that its dispatch stamps at kernel start and end
+ * (hipExtLaunchKernelGGL), and the launch first waits for its stream to drain, so that a recorded
+ * duration is the kernel's own and not the queueing behind its predecessor (tracing serializes
+ * the host with the stream; do not attach a trace while capturing a graph). bd_trace_get waits
+ * for the events of record i and returns the kernel name and its duration.
  * ---------------------------------------------------------------------------------------- */
 typedef struct bd_trace bd_trace;
 
