@@ -25,6 +25,17 @@ states. Sources (page title, section):
 * Block loop (Algorithm 1) -- Nemotron-TwoTower technical summary,
   §Generation: a block of S masked tokens is refined for T steps and then
   committed.
+* Context-tower update after a commit -- Nemotron-TwoTower technical summary,
+  §Architecture (the frozen context tower is a causal autoregressive model
+  over the prompt and the committed tokens, producing the KV cache) and
+  §Generation (once a block commits, the context tower takes in the new clean
+  tokens before the next block): a causal pass over the block (each new token
+  sees the prefix and the new tokens up to itself) and the append of the
+  block's keys and values to the cache.
+* Self-speculation (LinearSpec) -- Nemotron-Labs Diffusion page, decoding
+  modes: the same model drafts a block bidirectionally, then checks it
+  causally; the matching prefix is committed; lossless against AR decoding at
+  temperature 0.
 
 Readings where the pages are silent (all listed in the design doc):
 one softmax over prefix keys followed by block keys; every prefix key visible
@@ -34,7 +45,15 @@ maximum softmax probability at temperature 1; argmax ties -> lowest token
 index; commit iff p > gamma (strict) with gamma promoted from float32; when no
 masked position passes, the single most confident masked position commits
 (ties -> lowest position); at the last step every masked position commits;
-commits are final.
+commits are final. Causal pass: block key j is visible to block position s iff
+j <= s (all prefix keys stay visible). KV append: the block's rows go to cache
+positions len .. len+S-1 and len grows by S. Self-speculation: AR's choice for
+block position i is the argmax of the causal pass at position i-1 (for i = 0:
+the choice carried from the pass before); the committed run is the longest
+prefix of the draft equal to AR's choices, followed, when it is shorter than
+the block, by AR's own choice at the first mismatch (the token AR decoding
+would emit there, so the output stays identical to AR decoding and every
+verification commits at least one token).
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 things other than itself (library routines for special cases, closed forms,
@@ -85,9 +104,12 @@ def keys_values(k_blk, v_blk, k_cache, v_cache, prefix_len, b: int, g: int):
     return K, V
 
 
-def softmax_attention(Qr: np.ndarray, K: np.ndarray, V: np.ndarray, tau: float):
-    """O = softmax(tau * Qr K^T) V and LSE = ln sum exp(tau * Qr K^T), row-wise, float64."""
+def softmax_attention(Qr: np.ndarray, K: np.ndarray, V: np.ndarray, tau: float, visible=None):
+    """O = softmax(tau * Qr K^T) V and LSE = ln sum exp(tau * Qr K^T), row-wise, float64.
+    ``visible`` (rows x keys, bool) removes the invisible keys from each row's softmax."""
     s = tau * (Qr @ K.T)
+    if visible is not None:
+        s = np.where(visible, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
     z = e.sum(axis=1, keepdims=True)
@@ -96,14 +118,22 @@ def softmax_attention(Qr: np.ndarray, K: np.ndarray, V: np.ndarray, tau: float):
     return O, lse
 
 
+def causal_visible(S: int, n_prefix: int, rows_s: Sequence[int]):
+    """Visibility of the causal pass: rows at block positions rows_s see every prefix key and the
+    block keys j <= s."""
+    j = np.arange(n_prefix + S)
+    return np.stack([(j < n_prefix) | (j - n_prefix <= s) for s in rows_s])
+
+
 def attn_step(q, k_blk, v_blk, k_cache, v_cache, prefix_len, scale: Optional[float] = None,
-              active: Optional[Sequence[int]] = None):
+              active: Optional[Sequence[int]] = None, causal: bool = False):
     """One denoise-step attention for every (b, s, h).
 
     q [B,S,Hq,D]; k_blk, v_blk [B,S,Hkv,D]; k_cache, v_cache [B,Hkv,Lcap,D];
     prefix_len [B] -- all float64 (decode bf16 first). Returns O [B,S,Hq,D] and
     LSE [B,Hq,S] (float64). Sequences with ``active[b] == 0`` get NaN rows
-    (the step does not touch them)."""
+    (the step does not touch them). ``causal``: the context tower's pass over a
+    committed block (block key j visible to block position s iff j <= s)."""
     B, S, Hq, D = q.shape
     Hkv = k_blk.shape[2]
     tau = default_scale(D) if scale is None else float(np.float32(scale))
@@ -114,13 +144,14 @@ def attn_step(q, k_blk, v_blk, k_cache, v_cache, prefix_len, scale: Optional[flo
             continue
         for h in range(Hq):
             K, V = keys_values(k_blk, v_blk, k_cache, v_cache, prefix_len, b, kv_head_of(h, Hq, Hkv))
-            o, lse = softmax_attention(q[b, :, h, :], K, V, tau)
+            vis = causal_visible(S, int(prefix_len[b]), range(S)) if causal else None
+            o, lse = softmax_attention(q[b, :, h, :], K, V, tau, vis)
             O[b, :, h, :] = o
             L[b, h, :] = lse
     return O, L
 
 
-def attn_rows(q, k_blk, v_blk, k_cache, v_cache, prefix_len, rows: Iterable, scale=None):
+def attn_rows(q, k_blk, v_blk, k_cache, v_cache, prefix_len, rows: Iterable, scale=None, causal: bool = False):
     """Same definition for selected (b, s, h) triples only (full-size sampled checks).
 
     Inputs may be bf16 bit arrays (uint16) or float64; only the slabs needed
@@ -138,7 +169,8 @@ def attn_rows(q, k_blk, v_blk, k_cache, v_cache, prefix_len, rows: Iterable, sca
         K = np.concatenate([dec(k_cache[b, g, :n, :]), dec(k_blk[b, :, g, :])], axis=0)
         V = np.concatenate([dec(v_cache[b, g, :n, :]), dec(v_blk[b, :, g, :])], axis=0)
         Qr = np.stack([dec(q[b, s, h, :]) for (_, s, h) in lst])
-        o, lse = softmax_attention(Qr, K, V, tau)
+        vis = causal_visible(S, n, [s for (_, s, _) in lst]) if causal else None
+        o, lse = softmax_attention(Qr, K, V, tau, vis)
         for i, key in enumerate(lst):
             out[key] = (o[i], float(lse[i]))
     return out
@@ -294,6 +326,61 @@ def near_ties(p, mask, S, gamma, min_commit=True, commit_all=False, rel=NEAR_TIE
 # ----------------------------------------------------------------------------------------------
 # the T-step block loop
 # ----------------------------------------------------------------------------------------------
+# ----------------------------------------------------------------------------------------------
+# context-tower update after a commit, and self-speculation
+# ----------------------------------------------------------------------------------------------
+def kv_append(k_cache, v_cache, prefix_len, k_new, v_new, active: Optional[Sequence[int]] = None):
+    """Append the committed block: for every active sequence b and KV head g, rows
+    prefix_len[b] .. prefix_len[b]+S-1 of the cache become k_new[b, :, g, :] / v_new[b, :, g, :],
+    then prefix_len[b] += S. Returns new (k_cache, v_cache, prefix_len); inputs are not modified
+    (any dtype: the rows are copied bit for bit)."""
+    kc, vc, ln = np.array(k_cache, copy=True), np.array(v_cache, copy=True), np.array(prefix_len, copy=True)
+    B, S, Hkv, D = k_new.shape
+    for b in range(B):
+        if active is not None and not active[b]:
+            continue
+        n = int(ln[b])
+        if n + S > kc.shape[2]:
+            raise ValueError("append past the cache capacity")
+        for g in range(Hkv):
+            kc[b, g, n:n + S, :] = k_new[b, :, g, :]
+            vc[b, g, n:n + S, :] = v_new[b, :, g, :]
+        ln[b] = n + S
+    return kc, vc, ln
+
+
+def spec_accept(draft, first_choice, pass_argmax, S: int):
+    """Self-speculation check of drafted blocks against the causal pass over them.
+
+    draft [B*S] drafted tokens; first_choice [B] AR's choice for block position 0 (carried from
+    the pass before); pass_argmax [B*S] argmax of the causal pass at each block position (the
+    choice for the next position). AR's choice for position i: first_choice[b] for i = 0, else
+    pass_argmax[b*S + i - 1]. Returns dict(tokens [B*S] (committed positions filled, others
+    -1), n_commit [B], next_choice [B]: AR's choice for the position after the committed run when
+    the pass has seen every committed token (the whole draft accepted), else -1)."""
+    draft = np.asarray(draft, dtype=np.int64)
+    pa = np.asarray(pass_argmax, dtype=np.int64)
+    B = draft.size // S
+    tokens = np.full(B * S, -1, dtype=np.int32)
+    n_commit = np.zeros(B, dtype=np.int32)
+    next_choice = np.full(B, -1, dtype=np.int32)
+    for b in range(B):
+        k = 0
+        while k < S:
+            ar = int(first_choice[b]) if k == 0 else int(pa[b * S + k - 1])
+            if int(draft[b * S + k]) != ar:
+                break
+            tokens[b * S + k] = draft[b * S + k]
+            k += 1
+        if k < S:
+            tokens[b * S + k] = int(first_choice[b]) if k == 0 else int(pa[b * S + k - 1])
+            n_commit[b] = k + 1
+        else:
+            n_commit[b] = S
+            next_choice[b] = int(pa[b * S + S - 1])
+    return {"tokens": tokens, "n_commit": n_commit, "next_choice": next_choice}
+
+
 def denoise_block(T: int, t0: int, B: int, S: int, mask0, tokens0, step_inputs: Callable,
                   k_cache, v_cache, prefix_len, gamma: float, min_commit: bool = True,
                   final_commit_all: bool = True, logits_decode=None, scale=None):

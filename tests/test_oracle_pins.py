@@ -419,10 +419,125 @@ def _fails(fn, *a):
     return False
 
 
+# ------------------------------------------------------------ context-tower pass, append, LinearSpec
+def test_causal_pass_without_prefix_is_causal_attention():
+    # L = 0: block position s sees block keys 0..s -- torch's causal SDPA on the block alone.
+    q, kb, vb, kc, vc, lens = make_case(B=2, S=6, Hq=4, Hkv=4, D=8, lens=(0, 0), seed=21)
+    Oo, _ = O.attn_step(q, kb, vb, kc, vc, lens, causal=True)
+    for b in range(2):
+        ref = sdpa(q[b].transpose(1, 0, 2), kb[b].transpose(1, 0, 2), vb[b].transpose(1, 0, 2), is_causal=True,
+                   scale=O.default_scale(8))
+        np.testing.assert_allclose(Oo[b], ref.transpose(1, 0, 2), rtol=1e-12, atol=1e-13)
+
+
+def test_causal_pass_with_prefix_is_the_full_causal_sequence():
+    # [prefix ; block] under one causal mask: the block's rows are the causal pass over the block.
+    rng = np.random.default_rng(22)
+    H, D, L, S = 3, 8, 7, 5
+    xk, xv, xq = (rng.standard_normal((H, L + S, D)) for _ in range(3))
+    full = sdpa(xq, xk, xv, is_causal=True, scale=O.default_scale(D))
+    Oo, _ = O.attn_step(xq[:, L:].transpose(1, 0, 2)[None], xk[:, L:].transpose(1, 0, 2)[None],
+                        xv[:, L:].transpose(1, 0, 2)[None], xk[None, :, :L], xv[None, :, :L], np.array([L]),
+                        causal=True)
+    np.testing.assert_allclose(Oo[0], full[:, L:].transpose(1, 0, 2), rtol=1e-12, atol=1e-13)
+
+
+def test_causal_pass_is_incremental_decode_over_the_appended_cache():
+    # Row s of the causal pass equals a one-token step at position len + s over the cache into
+    # which block rows 0..s-1 were appended: appending the block is exact for what follows.
+    q, kb, vb, kc, vc, lens = make_case(B=2, S=5, Hq=4, Hkv=2, D=8, lens=(6, 3), seed=23, lcap=12)
+    Oc, Lc = O.attn_step(q, kb, vb, kc, vc, lens, causal=True)
+    for s in range(5):
+        kc2, vc2, ln2 = kc, vc, lens
+        if s:
+            kc2, vc2, ln2 = O.kv_append(kc, vc, lens, kb[:, :s], vb[:, :s])
+        o1, l1 = O.attn_step(q[:, s:s + 1], kb[:, s:s + 1], vb[:, s:s + 1], kc2, vc2, ln2)
+        np.testing.assert_allclose(o1[:, 0], Oc[:, s], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(l1[:, :, 0], Lc[:, :, s], rtol=1e-12, atol=1e-13)
+
+
+def test_last_causal_row_is_the_bidirectional_row():
+    q, kb, vb, kc, vc, lens = make_case(B=2, S=4, Hq=4, Hkv=2, D=8, lens=(5, 0), seed=24)
+    Oc, _ = O.attn_step(q, kb, vb, kc, vc, lens, causal=True)
+    Ob, _ = O.attn_step(q, kb, vb, kc, vc, lens)
+    np.testing.assert_array_equal(Oc[:, -1], Ob[:, -1])
+    assert not np.allclose(Oc[:, 0], Ob[:, 0])
+
+
+def test_kv_append_rows_and_lengths():
+    rng = np.random.default_rng(25)
+    B, Hkv, Lcap, D, S = 3, 2, 10, 4, 3
+    kc = rng.integers(0, 1 << 16, (B, Hkv, Lcap, D)).astype(np.uint16)
+    vc = rng.integers(0, 1 << 16, (B, Hkv, Lcap, D)).astype(np.uint16)
+    kn = rng.integers(0, 1 << 16, (B, S, Hkv, D)).astype(np.uint16)
+    vn = rng.integers(0, 1 << 16, (B, S, Hkv, D)).astype(np.uint16)
+    lens = np.array([0, 4, 7], dtype=np.int32)
+    k2, v2, l2 = O.kv_append(kc, vc, lens, kn, vn, active=[1, 0, 1])
+    np.testing.assert_array_equal(l2, [3, 4, 10])
+    for b, n in ((0, 0), (2, 7)):
+        for g in range(Hkv):
+            np.testing.assert_array_equal(k2[b, g, n:n + S], kn[b, :, g])
+            np.testing.assert_array_equal(v2[b, g, n:n + S], vn[b, :, g])
+            np.testing.assert_array_equal(k2[b, g, :n], kc[b, g, :n])
+            np.testing.assert_array_equal(k2[b, g, n + S:], kc[b, g, n + S:])
+    np.testing.assert_array_equal(k2[1], kc[1])
+    with pytest.raises(ValueError):
+        O.kv_append(kc, vc, np.array([8, 0, 0], dtype=np.int32), kn, vn)
+
+
+def test_spec_accept_cases():
+    S = 4
+    draft = np.array([5, 6, 7, 8,   1, 2, 3, 4,   3, 3, 3, 3])
+    first = np.array([5, 9, 3])
+    pa = np.array([6, 7, 8, 2,      2, 3, 4, 5,   3, 3, 3, 1])
+    r = O.spec_accept(draft, first, pa, S)
+    # seq 0: every draft token is AR's choice -> all commit, next choice from the last position
+    # seq 1: position 0 differs -> AR's own choice (9) commits alone
+    # seq 2: all equal -> all commit
+    np.testing.assert_array_equal(r["n_commit"], [4, 1, 4])
+    np.testing.assert_array_equal(r["tokens"], [5, 6, 7, 8, 9, -1, -1, -1, 3, 3, 3, 3])
+    np.testing.assert_array_equal(r["next_choice"], [2, -1, 1])
+    r = O.spec_accept(np.array([5, 6, 0, 8]), np.array([5]), np.array([6, 7, 8, 2]), S)
+    np.testing.assert_array_equal(r["tokens"], [5, 6, 7, -1])
+    assert r["n_commit"][0] == 3 and r["next_choice"][0] == -1
+
+
+def test_spec_accept_is_lossless_against_ar_decoding():
+    # A toy deterministic AR model (next token = hash of the last three tokens). Drafts with
+    # random corruptions, checked block by block with the causal pass simulated from the model,
+    # reproduce the model's own greedy decode exactly, and every check commits >= 1 token.
+    V, S, N = 11, 5, 60
+
+    def f(ctx):
+        return (7 * ctx[-1] + 3 * ctx[-2] + ctx[-3] * ctx[-1] + 5) % V
+
+    rng = np.random.default_rng(26)
+    ar = [1, 2, 3]
+    while len(ar) < 3 + N + S:
+        ar.append(f(ar))
+    out = [1, 2, 3]
+    while len(out) < 3 + N:
+        pos = len(out)
+        truth = ar[pos:pos + S]
+        draft = [t if rng.random() < 0.7 else int(rng.integers(V)) for t in truth]
+        ctx = list(out)
+        pa = []
+        for i in range(S):        # causal pass over the draft: the model's choice after draft[:i+1]
+            pa.append(f(ctx + draft[:i + 1]))
+        r = O.spec_accept(np.array(draft), np.array([f(ctx)]), np.array(pa), S)
+        n = int(r["n_commit"][0])
+        assert n >= 1
+        out += [int(t) for t in r["tokens"][:n]]
+        if draft == truth:
+            assert n == S and r["next_choice"][0] == f(out)
+    assert out[:3 + N] == ar[:3 + N]
+
+
 def test_planted_mistakes_are_caught(monkeypatch):
     """Plant plausible slips in the oracle (on the CPU) and check that some pin fails."""
     orig = {k: getattr(O, k) for k in ("kv_head_of", "default_scale", "vocab_reduce", "keys_values",
-                                       "softmax_attention", "merge_partials", "commit")}
+                                       "softmax_attention", "merge_partials", "commit", "causal_visible",
+                                       "kv_append", "spec_accept")}
 
     def check(name, bad, pins):
         monkeypatch.setattr(O, name, bad)
@@ -442,13 +557,15 @@ def test_planted_mistakes_are_caught(monkeypatch):
         return k_blk[b, :, g], v_blk[b, :, g]
     check("keys_values", no_prefix, [(test_one_token_block_is_causal_decode,)])
 
-    def transposed(Qr, K, V, tau):
-        o, l = orig["softmax_attention"](Qr, K, V, tau)
+    def transposed(Qr, K, V, tau, visible=None):
+        o, l = orig["softmax_attention"](Qr, K, V, tau, visible)
         return o[:, ::-1].copy(), l
     check("softmax_attention", transposed, [(test_no_prefix_is_plain_bidirectional_attention,)])
 
-    def no_max_sub(Qr, K, V, tau):
+    def no_max_sub(Qr, K, V, tau, visible=None):
         e = np.exp(tau * (Qr @ K.T))
+        if visible is not None:
+            e = np.where(visible, e, 0.0)
         z = e.sum(axis=1, keepdims=True)
         return (e / z) @ V, np.log(z[:, 0])
     check("softmax_attention", no_max_sub, [(test_closed_forms,)])
@@ -475,3 +592,27 @@ def test_planted_mistakes_are_caught(monkeypatch):
             orig["commit"](p[::-1].copy(), a[::-1].copy(), mask[::-1].copy(), tokens[::-1].copy(), S, gamma,
                            min_commit, commit_all)
     check("commit", last_fallback, [(test_commit_threshold_is_strict,), (test_commit_rule_cases,)])
+
+    def strict_causal(S, n_prefix, rows_s):
+        j = np.arange(n_prefix + S)
+        return np.stack([(j < n_prefix) | (j - n_prefix < max(s, 1)) for s in rows_s])
+    check("causal_visible", strict_causal, [(test_causal_pass_without_prefix_is_causal_attention,)])
+
+    def append_one_late(k_cache, v_cache, prefix_len, k_new, v_new, active=None):
+        kc, vc, ln = orig["kv_append"](k_cache, v_cache, np.asarray(prefix_len) + 1, k_new, v_new, active)
+        return kc, vc, ln - 1
+    check("kv_append", append_one_late, [(test_kv_append_rows_and_lengths,)])
+
+    def no_correction(draft, first_choice, pass_argmax, S):
+        r = orig["spec_accept"](draft, first_choice, pass_argmax, S)
+        for b in range(len(r["n_commit"])):
+            if r["n_commit"][b] < S or r["next_choice"][b] < 0:
+                r["n_commit"][b] -= 1
+        return r
+    check("spec_accept", no_correction, [(test_spec_accept_cases,)])
+
+    def unshifted(draft, first_choice, pass_argmax, S):
+        pa = np.asarray(pass_argmax).reshape(-1, S)
+        shifted = np.concatenate([pa[:, 1:], pa[:, -1:]], axis=1).reshape(-1)
+        return orig["spec_accept"](draft, first_choice, shifted, S)
+    check("spec_accept", unshifted, [(test_spec_accept_is_lossless_against_ar_decoding,)])
