@@ -50,9 +50,11 @@ def version() -> str:
     return _lib.load().bd_version().decode()
 
 
-def attn_desc(B, Hq, Hkv, D, S, prefix_capacity, max_prefix_len=None, softmax_scale=0.0, num_splits=0) -> AttnDesc:
+def attn_desc(B, Hq, Hkv, D, S, prefix_capacity, max_prefix_len=None, softmax_scale=0.0, num_splits=0,
+              causal=False) -> AttnDesc:
     return AttnDesc(B, Hq, Hkv, D, S, prefix_capacity,
-                    prefix_capacity if max_prefix_len is None else max_prefix_len, softmax_scale, num_splits)
+                    prefix_capacity if max_prefix_len is None else max_prefix_len, softmax_scale, num_splits,
+                    int(bool(causal)))
 
 
 def unmask_desc(B, S, V, row_stride=None, bf16=True, gamma=0.9, min_commit=True, commit_all=False) -> UnmaskDesc:
@@ -80,7 +82,7 @@ def _workspace(nbytes, device, workspace):
 
 
 def attn_step(q, k_blk, v_blk, k_cache, v_cache, prefix_len, active=None, out=None, lse=None, want_lse=True,
-              max_prefix_len=None, softmax_scale=0.0, num_splits=0, workspace=None, stream=None):
+              max_prefix_len=None, softmax_scale=0.0, num_splits=0, workspace=None, stream=None, causal=False):
     """bd_attn_step on torch tensors. q [B,S,Hq,D], k_blk/v_blk [B,S,Hkv,D], k_cache/v_cache
     [B,Hkv,Lcap,D] (bf16), prefix_len [B] int32, active [B] uint8 or None. Returns (out, lse)."""
     torch = _torch()
@@ -98,7 +100,7 @@ def attn_step(q, k_blk, v_blk, k_cache, v_cache, prefix_len, active=None, out=No
         raise ValueError("k_cache / v_cache must be [B, Hkv, Lcap, D]")
     if prefix_len.shape != (B,):
         raise ValueError("prefix_len must be [B]")
-    desc = attn_desc(B, Hq, Hkv, D, S, k_cache.shape[2], max_prefix_len, softmax_scale, num_splits)
+    desc = attn_desc(B, Hq, Hkv, D, S, k_cache.shape[2], max_prefix_len, softmax_scale, num_splits, causal)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -109,6 +111,61 @@ def attn_step(q, k_blk, v_blk, k_cache, v_cache, prefix_len, active=None, out=No
                               _ptr(prefix_len), _ptr(active), _ptr(out), _ptr(lse), _ptr(ws),
                               ws.numel() if ws is not None else 0, _stream(stream)), "bd_attn_step")
     return out, lse
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, prefix_len, active=None, max_prefix_len=None, stream=None):
+    """bd_kv_append on torch tensors: k_new/v_new [B,S,Hkv,D] bf16 go to cache rows
+    prefix_len[b] .. +S-1 of k_cache/v_cache [B,Hkv,Lcap,D]; prefix_len [B] int32 advances by S
+    (in place, for active sequences)."""
+    torch = _torch()
+    L = _lib.load()
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev_tensor(t, n, torch.bfloat16)
+    _dev_tensor(prefix_len, "prefix_len", torch.int32)
+    if active is not None:
+        _dev_tensor(active, "active", torch.uint8)
+    B, S, Hkv, D = k_new.shape
+    if v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must have the same shape [B, S, Hkv, D]")
+    if k_cache.shape[0] != B or k_cache.shape[1] != Hkv or k_cache.shape[3] != D or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache / v_cache must be [B, Hkv, Lcap, D]")
+    Lcap = k_cache.shape[2]
+    mpl = Lcap - S if max_prefix_len is None else max_prefix_len
+    desc = attn_desc(B, Hkv, Hkv, D, S, Lcap, mpl)
+    _lib.check(L.bd_kv_append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(prefix_len), _ptr(active), _stream(stream)), "bd_kv_append")
+
+
+def spec_verify(logits, draft, first_choice, block_len, vocab=None, tokens=None, n_commit=None, next_choice=None,
+                workspace=None, stream=None):
+    """bd_spec_verify on torch tensors: logits [B*S, row_stride] (bf16 or float32) of the causal pass
+    over the drafted block, draft [B*S] int32, first_choice [B] int32. Returns dict(tokens,
+    n_commit, next_choice)."""
+    torch = _torch()
+    L = _lib.load()
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("logits must be bfloat16 or float32")
+    _dev_tensor(logits, "logits")
+    _dev_tensor(draft, "draft", torch.int32)
+    _dev_tensor(first_choice, "first_choice", torch.int32)
+    rows, stride = logits.shape
+    if rows % block_len != 0 or draft.numel() != rows:
+        raise ValueError("logits rows and draft must be B * block_len")
+    B = rows // block_len
+    if first_choice.numel() != B:
+        raise ValueError("first_choice must hold one entry per sequence")
+    V = stride if vocab is None else vocab
+    desc = unmask_desc(B, block_len, V, stride, bf16=logits.dtype == torch.bfloat16)
+    dev = logits.device
+    tokens = torch.empty(rows, dtype=torch.int32, device=dev) if tokens is None else tokens
+    n_commit = torch.empty(B, dtype=torch.int32, device=dev) if n_commit is None else n_commit
+    next_choice = torch.empty(B, dtype=torch.int32, device=dev) if next_choice is None else next_choice
+    nbytes = L.bd_unmask_workspace_bytes(ctypes.byref(desc))
+    ws = _workspace(nbytes, dev, workspace)
+    _lib.check(L.bd_spec_verify(ctypes.byref(desc), _ptr(logits), _ptr(draft), _ptr(first_choice), _ptr(tokens),
+                                _ptr(n_commit), _ptr(next_choice), _ptr(ws), ws.numel() if ws is not None else 0,
+                                _stream(stream)), "bd_spec_verify")
+    return {"tokens": tokens, "n_commit": n_commit, "next_choice": next_choice}
 
 
 def confidence_unmask(logits, mask, tokens, block_len, gamma, vocab=None, min_commit=True, commit_all=False,

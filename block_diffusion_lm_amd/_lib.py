@@ -23,6 +23,7 @@ class AttnDesc(ctypes.Structure):
         ("max_prefix_len", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float),
         ("num_splits", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
     ]
 
 
@@ -60,6 +61,7 @@ EXPORTS = [
     "bd_attn_workspace_bytes", "bd_attn_step", "bd_unmask_workspace_bytes", "bd_confidence_unmask",
     "bd_denoise_workspace_bytes", "bd_denoise_block", "bd_last_error", "bd_trace_create", "bd_trace_destroy",
     "bd_trace_attach", "bd_trace_clear", "bd_trace_count", "bd_trace_get", "bd_version", "bd_table_hooks",
+    "bd_kv_append", "bd_spec_verify",
 ]
 
 _lib = None
@@ -91,6 +93,10 @@ def load() -> ctypes.CDLL:
     L.bd_denoise_block.argtypes = [P(AttnDesc), P(UnmaskDesc), i32, i32, P(StepHooks), vp, vp, vp, vp, vp, vp, vp,
                                    vp, vp, sz, vp]
     L.bd_denoise_block.restype = ctypes.c_int
+    L.bd_kv_append.argtypes = [P(AttnDesc), vp, vp, vp, vp, vp, vp, vp]
+    L.bd_kv_append.restype = ctypes.c_int
+    L.bd_spec_verify.argtypes = [P(UnmaskDesc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.bd_spec_verify.restype = ctypes.c_int
     L.bd_table_hooks.argtypes = [P(StepTable), P(StepHooks)]
     L.bd_table_hooks.restype = ctypes.c_int
     L.bd_last_error.argtypes = []

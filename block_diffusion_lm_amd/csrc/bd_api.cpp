@@ -82,6 +82,7 @@ bd_status check_attn_desc(const bd_attn_desc* d) {
     return fail(BD_EINVAL, "max_prefix_len must be in [0, prefix_capacity]");
   if (!std::isfinite(d->softmax_scale)) return fail(BD_EINVAL, "softmax_scale must be finite");
   if (d->num_splits < 0) return fail(BD_EINVAL, "num_splits must be >= 0");
+  if (d->causal != 0 && d->causal != 1) return fail(BD_EINVAL, "causal must be 0 or 1");
   const int64_t rows = (int64_t)d->block_len * (d->n_q_heads / d->n_kv_heads);
   if (rows > (1 << 20)) return fail(BD_EUNSUPPORTED, "too many query rows per KV head");
   return BD_OK;
@@ -179,6 +180,7 @@ bd_status run_attn(const bd_attn_desc* d, const bd::AttnPlan& plan, const void* 
   const float tau = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
   a.scale_log2 = tau * 1.4426950408889634f;
   a.direct = plan.direct ? 1 : 0;
+  a.causal = d->causal;
   bd_status st = traced("attn_split", stream, [&](const bd::Launch& l) { return bd::launch_attn_split(plan, a, l); });
   if (st != BD_OK || plan.direct) return st;
   return traced("attn_merge", stream, [&](const bd::Launch& l) { return bd::launch_attn_merge(plan, a, l); });
@@ -320,6 +322,75 @@ bd_status bd_confidence_unmask(const bd_unmask_desc* desc, const void* logits, u
   if (st != BD_OK) return st;
   return run_unmask(desc, plan, logits, mask, tokens, conf, argmax, n_commit, workspace, desc->commit_all, 0,
                     nullptr, nullptr, static_cast<hipStream_t>(stream));
+}
+
+bd_status bd_kv_append(const bd_attn_desc* desc, const void* k_new, const void* v_new, void* k_cache,
+                       void* v_cache, int32_t* prefix_len, const uint8_t* active, void* stream) {
+  bd_status st = check_attn_desc(desc);
+  if (st != BD_OK) return st;
+  if (desc->max_prefix_len + desc->block_len > desc->prefix_capacity)
+    return fail(BD_EINVAL, "append would pass the cache capacity: max_prefix_len (%lld) + block_len (%d) > "
+                "prefix_capacity (%lld)", (long long)desc->max_prefix_len, desc->block_len,
+                (long long)desc->prefix_capacity);
+  const void* req[] = {k_new, v_new, k_cache, v_cache};
+  const char* names[] = {"k_new", "v_new", "k_cache", "v_cache"};
+  for (int i = 0; i < 4; ++i) {
+    if (!req[i]) return fail(BD_EINVAL, "%s is NULL", names[i]);
+    if (!aligned(req[i], 16)) return fail(BD_EINVAL, "%s is not 16-byte aligned", names[i]);
+  }
+  if (!prefix_len || !aligned(prefix_len, 4)) return fail(BD_EINVAL, "prefix_len is NULL or not 4-byte aligned");
+  bd::AppendArgs a{};
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.k_cache = static_cast<uint16_t*>(k_cache);
+  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.prefix_len = prefix_len;
+  a.active = active;
+  a.B = desc->batch;
+  a.S = desc->block_len;
+  a.Hkv = desc->n_kv_heads;
+  a.D = desc->head_dim;
+  a.lcap = desc->prefix_capacity;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = traced("kv_append", s, [&](const bd::Launch& l) { return bd::launch_kv_append(a, l); });
+  if (st != BD_OK) return st;
+  return traced("len_advance", s, [&](const bd::Launch& l) { return bd::launch_len_advance(a, l); });
+}
+
+bd_status bd_spec_verify(const bd_unmask_desc* desc, const void* logits, const int32_t* draft,
+                         const int32_t* first_choice, int32_t* tokens, int32_t* n_commit, int32_t* next_choice,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  bd_status st = check_unmask_desc(desc);
+  if (st != BD_OK) return st;
+  if (!logits || !aligned(logits, 16)) return fail(BD_EINVAL, "logits is NULL or not 16-byte aligned");
+  const void* req[] = {draft, first_choice, tokens, n_commit, next_choice};
+  const char* names[] = {"draft", "first_choice", "tokens", "n_commit", "next_choice"};
+  for (int i = 0; i < 5; ++i)
+    if (!req[i] || !aligned(req[i], 4)) return fail(BD_EINVAL, "%s is NULL or not 4-byte aligned", names[i]);
+  bd::UnmaskPlan plan;
+  plan_unmask(desc, &plan);
+  st = check_ws(workspace, workspace_bytes, plan.bytes);
+  if (st != BD_OK) return st;
+  bd::UnmaskArgs a{};
+  a.logits = logits;
+  a.is_bf16 = desc->logits_dtype == BD_BF16;
+  a.row_stride = desc->row_stride;
+  a.vocab = desc->vocab;
+  a.B = desc->batch;
+  a.S = desc->block_len;
+  a.mask = nullptr;   // every row
+  a.tokens = tokens;
+  a.n_commit = n_commit;
+  a.part = static_cast<float*>(workspace);
+  a.vsplit = plan.vsplit;
+  a.slice = plan.slice;
+  a.draft = draft;
+  a.first_choice = first_choice;
+  a.next_choice = next_choice;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = traced("vocab_reduce", s, [&](const bd::Launch& l) { return bd::launch_vocab_reduce(a, l); });
+  if (st != BD_OK) return st;
+  return traced("spec_accept", s, [&](const bd::Launch& l) { return bd::launch_spec_accept(a, l); });
 }
 
 size_t bd_denoise_workspace_bytes(const bd_attn_desc* attn, const bd_unmask_desc* unmask) {

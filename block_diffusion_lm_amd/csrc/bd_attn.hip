@@ -400,15 +400,24 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) sacc[rb] = mfma32(kf[kstep], qf[rb][kstep], sacc[rb]);
   };
-  // keys past the chunk end do not exist for this item (a block with `keys` < 32 existing keys)
-  auto mask_tail = [&](f32x16 (&sacc)[RB], int keys) {
-    if (keys < 32) {
-      const int lim = keys - 4 * half;   // register r holds key 8 (r / 4) + 4 half + r % 4
+  // Keys past the chunk end do not exist for this item (the block starting at absolute key key0
+  // has `keys` < 32 existing keys); in the causal pass, block key j (absolute key len + j) is
+  // invisible to block position s when j > s. Only tiles at a chunk end or holding block keys
+  // take the branch.
+  auto mask_keys = [&](f32x16 (&sacc)[RB], int64_t key0, int keys) {
+    const bool causal_here = a.causal && key0 + 32 > len;
+    if (keys < 32 || causal_here) {
+      const int lim = keys - 4 * half;   // register r holds key key0 + 8 (r / 4) + 4 half + r % 4
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + (r & 3) >= lim)
+      for (int rb = 0; rb < RB; ++rb) {
+        // last visible register offset of this lane's row in the causal pass
+        const int64_t vis = causal_here ? len + (row0 + rb * 32 + lrow) / a.group - key0 - 4 * half : (int64_t)64;
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) sacc[rb][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int off = 8 * (r >> 2) + (r & 3);
+          if (off >= lim || off > vis) sacc[rb][r] = -INFINITY;
+        }
+      }
     }
   };
   // block row maxima in log2 units
@@ -431,7 +440,9 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const float mnew = live && mx[rb] > m_run[rb] + kLazyRescale ? mx[rb] : m_run[rb];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - mnew);   // exp2(-inf) = 0
+        // exp2(-inf) = 0 when the first visible keys arrive; a row whose max did not move (possibly
+        // still -inf: no visible key yet in the causal pass) keeps its accumulators as they are
+        const float alpha = mnew == m_run[rb] ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - mnew);
         l_run[rb] *= alpha;
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
@@ -448,7 +459,8 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
       bf16x8 pf[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const float mneg = -m_run[rb];
+        // no visible key yet for this row (causal pass): every P is 0, not exp2(nan)
+        const float mneg = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
 #pragma unroll
         for (int i = 0; i < 8; ++i) pf[rb][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[rb][8 * e + i], sc, mneg));
         float ls = l_run[rb];
@@ -504,7 +516,7 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
       bf16x8 kf[G::KS];
       load_k(st, 1, kf);
       read_vt<D, 0>(vaddr, vf);
-      mask_tail(s_even, min(valid, 32));
+      mask_keys(s_even, k_begin + (int64_t)t * G::KT, min(valid, 32));
       qk(kf, s_odd);
       row_max(s_even, mx);
       rescale(mx, true);
@@ -520,7 +532,7 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
       bf16x8 kf[G::KS];
       if constexpr (NSTAGE >= 3) load_k((t + 1) % NSTAGE, 0, kf);
       read_vt<D, 32 * G::VROW>(vaddr, vf);
-      mask_tail(s_odd, max(valid - 32, 0));
+      mask_keys(s_odd, k_begin + (int64_t)t * G::KT + 32, max(valid - 32, 0));
       if constexpr (NSTAGE < 3) {
         wait_tile(min(NSTAGE - 2, ntiles - 2 - t));
         if (t + NSTAGE < ntiles) issue_tile(st, k_begin + (int64_t)(t + NSTAGE) * G::KT);

@@ -69,6 +69,7 @@ struct AttnArgs {
   int nsplit, row_tiles;
   float scale_log2;   // tau * log2(e)
   int direct;
+  int causal;         // 1: block key j is visible to block position s only when j <= s
 };
 
 hipError_t launch_attn_split(const AttnPlan& plan, const AttnArgs& a, const Launch& l);
@@ -103,10 +104,32 @@ struct UnmaskArgs {
   int step;
   int32_t* steps_used;          // [B]: set to step+1 where the sequence had a masked position
   uint8_t* active_next;         // [B]: whether a masked position remains after the commit
+  // self-speculation check (mask == nullptr: every row is reduced)
+  const int32_t* draft;         // [B*S]
+  const int32_t* first_choice;  // [B]
+  int32_t* next_choice;         // [B]
 };
 
 hipError_t launch_vocab_reduce(const UnmaskArgs& a, const Launch& l);
 hipError_t launch_commit(const UnmaskArgs& a, const Launch& l);
+hipError_t launch_spec_accept(const UnmaskArgs& a, const Launch& l);
 hipError_t launch_loop_init(const uint8_t* mask, int B, int S, uint8_t* active, int32_t* steps_used, const Launch& l);
+
+// ---------------------------------------------------------------------------------------------
+// prefix cache append
+// ---------------------------------------------------------------------------------------------
+struct AppendArgs {
+  const uint16_t* k_new;   // [B, S, Hkv, D]
+  const uint16_t* v_new;
+  uint16_t* k_cache;       // [B, Hkv, Lcap, D]
+  uint16_t* v_cache;
+  int32_t* prefix_len;     // [B]
+  const uint8_t* active;   // [B] or nullptr
+  int B, S, Hkv, D;
+  int64_t lcap;
+};
+
+hipError_t launch_kv_append(const AppendArgs& a, const Launch& l);
+hipError_t launch_len_advance(const AppendArgs& a, const Launch& l);
 
 }  // namespace bd

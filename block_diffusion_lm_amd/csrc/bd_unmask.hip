@@ -92,7 +92,7 @@ __device__ void commit_sequence(const UnmaskArgs& a, int b);
 __global__ __launch_bounds__(256) void vocab_reduce_kernel(UnmaskArgs a) {
   const int64_t row = blockIdx.x / a.vsplit;
   const int part = (int)(blockIdx.x % a.vsplit);
-  if (a.mask[row]) reduce_slice(a, row, part);   // uniform per workgroup
+  if (!a.mask || a.mask[row]) reduce_slice(a, row, part);   // uniform per workgroup
 }
 
 __device__ void reduce_slice(const UnmaskArgs& a, int64_t row, int part) {
@@ -204,6 +204,33 @@ __device__ void commit_sequence(const UnmaskArgs& a, int b) {
 
 __global__ __launch_bounds__(64) void commit_kernel(UnmaskArgs a) { commit_sequence(a, blockIdx.x); }
 
+// Self-speculation check of sequence b by one wave (lane = block position): AR's choice for
+// position s is first_choice[b] (s = 0) or the argmax of row b*S + s - 1; the committed run is the
+// longest prefix of the draft equal to those choices, then AR's choice at the first mismatch.
+__global__ __launch_bounds__(64) void spec_accept_kernel(UnmaskArgs a) {
+  const int b = blockIdx.x;
+  const int s = threadIdx.x & 63;
+  const bool in = s < a.S;
+  const int64_t r = (int64_t)b * a.S + s;
+  // argmax of row r (the choice for position s + 1)
+  int choice_next = -1;
+  if (in) {
+    const float* pp = a.part + r * a.vsplit * 3;
+    Red st{pp[0], __float_as_int(pp[1]), pp[2]};
+    for (int c = 1; c < a.vsplit; ++c) st = combine(st, Red{pp[3 * c], __float_as_int(pp[3 * c + 1]), pp[3 * c + 2]});
+    choice_next = st.idx;
+  }
+  // AR's choice for position s: lane s - 1's row argmax, lane 0 takes first_choice[b]
+  const int up = __shfl_up(choice_next, 1, 64);
+  const int ar = s == 0 ? a.first_choice[b] : up;
+  const bool match = in && a.draft[r] == ar;
+  const uint64_t miss = __ballot(in && !match);
+  const int k = miss ? __builtin_ctzll(miss) : a.S;   // accepted run length
+  if (in) a.tokens[r] = s < k ? a.draft[r] : (s == k ? ar : -1);
+  if (s == 0) a.n_commit[b] = k < a.S ? k + 1 : a.S;
+  if (in && s == a.S - 1) a.next_choice[b] = k == a.S ? choice_next : -1;
+}
+
 __global__ __launch_bounds__(64) void loop_init_kernel(const uint8_t* mask, int S, uint8_t* active,
                                                        int32_t* steps_used) {
   const int b = blockIdx.x;
@@ -225,6 +252,10 @@ hipError_t launch_vocab_reduce(const UnmaskArgs& a, const Launch& l) {
 
 hipError_t launch_commit(const UnmaskArgs& a, const Launch& l) {
   return launch_kernel(commit_kernel, dim3((unsigned)a.B), dim3(64), l, a);
+}
+
+hipError_t launch_spec_accept(const UnmaskArgs& a, const Launch& l) {
+  return launch_kernel(spec_accept_kernel, dim3((unsigned)a.B), dim3(64), l, a);
 }
 
 hipError_t launch_loop_init(const uint8_t* mask, int B, int S, uint8_t* active, int32_t* steps_used, const Launch& l) {

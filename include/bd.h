@@ -21,6 +21,13 @@
  *  - Hybrid Block Diffusion with Partial Bidirectionality summary, technical
  *    §Method: the prefix cache is a function of the clean prefix only, so the
  *    step never writes it.
+ *  - Nemotron-TwoTower technical summary, §Architecture and §Generation: the
+ *    frozen context tower is a causal AR model over the committed tokens;
+ *    after a block commits it takes in the new clean tokens (bd_attn_desc's
+ *    causal mode, bd_kv_append).
+ *  - Nemotron-Labs Diffusion page, decoding modes (self-speculation,
+ *    LinearSpec): a block drafted bidirectionally is checked causally and its
+ *    matching prefix commits (bd_spec_verify).
  *
  * Conventions (every entry point):
  *  - Pointers are DEVICE pointers unless marked (host). The caller owns every
@@ -72,6 +79,10 @@ typedef enum { BD_BF16 = 0, BD_F32 = 1 } bd_dtype;
  * mask inside the block (every block position sees every other) and every
  * prefix key is visible to every block query. Positions are not applied here
  * (rotary embeddings, if any, are already in q and k).
+ *
+ * Causal mode (desc.causal = 1): the context tower's pass over a committed
+ * block, or the causal check of a drafted block -- block key j is visible to
+ * block position s only when j <= s (prefix keys stay visible to all).
  * ---------------------------------------------------------------------------------------- */
 typedef struct {
   int32_t batch;            /* B >= 1 */
@@ -83,6 +94,7 @@ typedef struct {
   int64_t max_prefix_len;   /* host upper bound on every prefix_len[b]; 0 .. Lcap; used to plan the split */
   float softmax_scale;      /* tau; <= 0 selects 1/sqrt(D) computed in float32 */
   int32_t num_splits;       /* 0 = automatic; > 0 forces the number of key chunks per (b, KV head) */
+  int32_t causal;           /* 0: bidirectional block (denoiser); 1: causal within the block */
 } bd_attn_desc;
 
 /* Workspace bytes bd_attn_step needs for this descriptor (0 on an invalid descriptor). */
@@ -105,6 +117,25 @@ bd_status bd_attn_step(const bd_attn_desc* desc,
                        const int32_t* prefix_len, const uint8_t* active,
                        void* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Context-tower update after a commit: append the committed block to the prefix cache
+ *
+ * For every active sequence b and KV head g:
+ *   k_cache[b, g, prefix_len[b] + s, :] = k_new[b, s, g, :]   (s = 0 .. S-1; likewise v)
+ * then prefix_len[b] += S. The rows are copied bit for bit; nothing else in the caches is
+ * written. k_new / v_new are the committed block's keys and values from the context tower's
+ * causal pass (bd_attn_step with desc.causal = 1 over the same block).
+ * desc: the attention descriptor (batch, n_kv_heads, head_dim, block_len = S, prefix_capacity,
+ *       max_prefix_len); max_prefix_len + S must not exceed prefix_capacity (BD_EINVAL otherwise),
+ *       and prefix_len[b] <= max_prefix_len is the device-side precondition as for bd_attn_step.
+ *       Afterwards max_prefix_len + S bounds the new lengths.
+ * k_new, v_new: bf16 [B, S, Hkv, D] (read only); k_cache, v_cache: bf16 [B, Hkv, Lcap, D] (rows
+ *       prefix_len[b] .. prefix_len[b]+S-1 written); prefix_len: int32 [B] (read, then advanced);
+ * active: uint8 [B] or NULL (all). Inactive sequences are untouched. No workspace. */
+bd_status bd_kv_append(const bd_attn_desc* desc, const void* k_new, const void* v_new,
+                       void* k_cache, void* v_cache, int32_t* prefix_len, const uint8_t* active,
+                       void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Confidence unmasking
@@ -142,6 +173,29 @@ bd_status bd_confidence_unmask(const bd_unmask_desc* desc, const void* logits,
                                uint8_t* mask, int32_t* tokens,
                                float* conf, int32_t* argmax, int32_t* n_commit,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Self-speculation check (LinearSpec): commit the prefix of a drafted block that AR decoding
+ * would produce
+ *
+ * logits are the causal pass over the drafted block (bd_attn_step with desc.causal = 1, then
+ * the model's head): row b*S + i predicts block position i + 1. For every row,
+ * c_r = min{ j : l_rj = max_j l_rj } (lowest index on ties). AR's choice for block position i of
+ * sequence b is first_choice[b] for i = 0 (carried from the pass before) and c_{b*S+i-1} for
+ * i >= 1. With k = the length of the longest prefix of draft[b*S ..] equal to AR's choices:
+ *   tokens[b*S + i] = draft[b*S + i] for i < k; tokens[b*S + k] = AR's choice at k if k < S;
+ *   every other position of the block gets -1;
+ *   n_commit[b] = min(k + 1, S)  (>= 1: AR's own choice at the first mismatch commits, so the
+ *                                 output is exactly AR decoding's at temperature 0);
+ *   next_choice[b] = c_{b*S+S-1} if k == S (AR's choice after the block), else -1 (the pass has
+ *                    not seen the corrected token; the next pass provides it).
+ * desc: batch, block_len (S), vocab, row_stride, logits_dtype (gamma, min_commit, commit_all are
+ *       not used). draft, first_choice: int32 [B*S], [B] (read only); tokens: int32 [B*S],
+ *       n_commit, next_choice: int32 [B] (written). workspace: >= bd_unmask_workspace_bytes(desc).
+ * Every row of the logits is read once (HBM-bound like the confidence pass). */
+bd_status bd_spec_verify(const bd_unmask_desc* desc, const void* logits, const int32_t* draft,
+                         const int32_t* first_choice, int32_t* tokens, int32_t* n_commit,
+                         int32_t* next_choice, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * The T-step block loop (Algorithm 1's inner loop)

@@ -64,6 +64,7 @@ def call_attn(L, d, ptr=16 * 1024, ws=None, nbytes=None):
     ("prefix_capacity", 0, _lib.BD_EINVAL),
     ("num_splits", -1, _lib.BD_EINVAL),
     ("softmax_scale", math.nan, _lib.BD_EINVAL),
+    ("causal", 2, _lib.BD_EINVAL),
 ])
 def test_attn_descriptor_validation(L, field, value, status):
     d = good_attn()
@@ -165,3 +166,35 @@ def test_trace_lifecycle_without_gpu(L):
     assert L.bd_trace_create(0, ctypes.byref(h)) == _lib.BD_EINVAL
     assert L.bd_trace_count(None) == 0
     assert L.bd_trace_get(None, 0, None, None) == _lib.BD_EINVAL
+
+
+def test_kv_append_validation(L):
+    d = good_attn()
+    d.max_prefix_len = d.prefix_capacity - d.block_len + 1          # one row past the capacity
+    p = ctypes.c_void_p(4096)
+    assert L.bd_kv_append(ctypes.byref(d), p, p, p, p, p, None, None) == _lib.BD_EINVAL
+    assert b"capacity" in L.bd_last_error()
+    d.max_prefix_len = d.prefix_capacity - d.block_len
+    for i in range(5):
+        a = [p] * 5
+        a[i] = None
+        assert L.bd_kv_append(ctypes.byref(d), *a, None, None) == _lib.BD_EINVAL
+    a = [p] * 5
+    a[0] = ctypes.c_void_p(4096 + 8)
+    assert L.bd_kv_append(ctypes.byref(d), *a, None, None) == _lib.BD_EINVAL
+    d.head_dim = 96
+    assert L.bd_kv_append(ctypes.byref(d), *([p] * 5), None, None) == _lib.BD_EUNSUPPORTED
+
+
+def test_spec_verify_validation(L):
+    d = good_unmask()
+    nb = L.bd_unmask_workspace_bytes(ctypes.byref(d))
+    p = ctypes.c_void_p(4096)
+    for i in range(6):
+        a = [p] * 6
+        a[i] = None
+        assert L.bd_spec_verify(ctypes.byref(d), *a, p, nb, None) == _lib.BD_EINVAL
+    assert L.bd_spec_verify(ctypes.byref(d), ctypes.c_void_p(4100), *([p] * 5), p, nb, None) == _lib.BD_EINVAL
+    assert L.bd_spec_verify(ctypes.byref(d), *([p] * 6), p, nb - 1, None) == _lib.BD_EWORKSPACE
+    d.vocab = 0
+    assert L.bd_spec_verify(ctypes.byref(d), *([p] * 6), p, nb, None) == _lib.BD_EINVAL
