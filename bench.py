@@ -92,6 +92,95 @@ def cpu_baseline(w, inputs, logits0, mask0, budget_s=20.0):
             "unmask_positions_per_s": n / t_um if t_um > 0 else None}
 
 
+def row_figures(args, w, bd, torch, dev, recs, steps_used, commits, mask0, lens, ad, ws, dq, dlog, caches, lens_d,
+                is_bf16, T):
+    """Per-row kernel durations (trace events) with their algorithmic bytes and HBM fraction.
+
+    Rows of the step, from the traced loop region, over the steps in which every sequence is
+    active: attn_split (K, V, Q read), attn_merge (the split partials read back, the output
+    written), vocab_reduce (the masked rows' logits), commit (latency only). Rows after the step,
+    each timed on its own with the same trace (5 launches, first dropped): the context tower's
+    causal pass over the block (bd_attn_step, causal), the append of the block to a cache
+    (bd_kv_append), the self-speculation check of a drafted block (bd_spec_verify)."""
+    per = {}
+    for name, ms in recs:
+        per.setdefault(name, []).append(ms)
+    # the loop enqueues all T steps (the early exit happens on the device), so every kernel of the
+    # step has T launches per call; step t is full when every sequence is still active at t
+    full = [t for t in range(T) if (steps_used > t).all()]
+    lg_bytes = 2 if is_bf16 else 4
+    out_bytes = w.B * w.S * w.Hq * w.D * 2
+    fl, kv, qb = attn_units(w, lens, np.ones(w.B, bool))
+    remaining = mask0.reshape(w.B, w.S).sum(axis=1).astype(np.int64)
+    masked_at = []
+    for t in range(T):
+        masked_at.append(int(remaining.sum()))
+        remaining -= commits[t]
+    part_bytes = bd.attn_workspace_bytes(ad)
+
+    def pick(name, ts):
+        v = per.get(name, [])
+        return [v[c * T + t] for c in range(len(v) // T) for t in ts]
+
+    def fig(ms_list, nbytes):
+        if not ms_list:
+            return None
+        avg = float(np.mean(ms_list))
+        r = {"avg_us": round(avg * 1e3, 2), "launches": len(ms_list)}
+        if nbytes:
+            gbs = nbytes / (avg * 1e-3) / 1e9
+            r.update({"bytes_per_launch": int(nbytes), "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+        return r
+
+    rows = {"attn_split": fig(pick("attn_split", full), kv + qb),
+            "attn_merge": fig(pick("attn_merge", full), part_bytes + out_bytes),
+            "vocab_reduce": fig(pick("vocab_reduce", [0]), masked_at[0] * w.V * lg_bytes),
+            "commit": fig(pick("commit", full), None)}
+
+    # rows after the step, each on its own
+    kc, vc = caches[0]
+    q, kb, vb = dq[0]
+    tr = bd.Trace(capacity=64)
+    with tr:
+        for _ in range(5):
+            bd.attn_step(q, kb, vb, kc, vc, lens_d, max_prefix_len=w.max_prefix_len, causal=True, want_lse=False,
+                         workspace=ws)
+    cp = {}
+    for name, ms in tr.records():
+        cp.setdefault(name, []).append(ms)
+    tr.clear()
+    ctx = [a + b for a, b in zip(cp.get("attn_split", [])[1:], cp.get("attn_merge", [0] * 5)[1:])]
+    rows["context_pass"] = fig(ctx, kv + qb + out_bytes)
+    kc_s = torch.zeros((w.B, w.Hkv, w.S, w.D), dtype=torch.bfloat16, device=dev)
+    vc_s = torch.zeros_like(kc_s)
+    len_s = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    with tr:
+        for _ in range(5):
+            len_s.zero_()
+            bd.kv_append(kb, vb, kc_s, vc_s, len_s, max_prefix_len=0)
+    ap = {}
+    for name, ms in tr.records():
+        ap.setdefault(name, []).append(ms)
+    tr.clear()
+    app = [a + b for a, b in zip(ap.get("kv_append", [])[1:], ap.get("len_advance", [])[1:])]
+    rows["kv_append"] = fig(app, 2 * 2 * w.B * w.S * w.Hkv * w.D * 2)
+    draft = torch.zeros(w.B * w.S, dtype=torch.int32, device=dev)
+    first = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    ws_u = torch.empty(max(bd.unmask_workspace_bytes(bd.unmask_desc(w.B, w.S, w.V, None, is_bf16)), 1),
+                       dtype=torch.uint8, device=dev)
+    with tr:
+        for _ in range(5):
+            bd.spec_verify(dlog[0], draft, first, w.S, vocab=w.V, workspace=ws_u)
+    sv = {}
+    for name, ms in tr.records():
+        sv.setdefault(name, []).append(ms)
+    tr.close()
+    spec = [a + b for a, b in zip(sv.get("vocab_reduce", [])[1:], sv.get("spec_accept", [])[1:])]
+    rows["spec_verify"] = fig(spec, w.B * w.S * w.V * lg_bytes)
+    torch.cuda.synchronize()
+    return rows
+
+
 def measured_traffic(kernel_source: str):
     """HBM traffic per launch of the attention split kernel from the committed counter summary
     (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a plain copy kernel), or None when the summary
@@ -284,6 +373,8 @@ def main():
                      "traffic": measured_traffic(os.path.join(ROOT, "block_diffusion_lm_amd", "csrc", "bd_attn.hip")),
                      "algorithmic_bytes_per_launch": round(bytes_per_launch)},
     }
+    line["rows"] = row_figures(args, w, bd, torch, dev, recs, steps_used, commits, mask0, lens, ad, ws, dq, dlog,
+                               caches, lens_d, is_bf16, T)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, inp0, logits_np[0], mask0, args.cpu_budget)
