@@ -36,6 +36,10 @@ states. Sources (page title, section):
   modes: the same model drafts a block bidirectionally, then checks it
   causally; the matching prefix is committed; lossless against AR decoding at
   temperature 0.
+* Adaptive loop halting -- Technical summary: LoopMDM, §Adaptive inference:
+  the looped mid-block stops when the relative change of the hidden state
+  between consecutive loop iterations falls below epsilon, or when the
+  iteration budget is reached.
 
 Readings where the pages are silent (all listed in the design doc):
 one softmax over prefix keys followed by block keys; every prefix key visible
@@ -53,7 +57,10 @@ the choice carried from the pass before); the committed run is the longest
 prefix of the draft equal to AR's choices, followed, when it is shorter than
 the block, by AR's own choice at the first mismatch (the token AR decoding
 would emit there, so the output stays identical to AR decoding and every
-verification commits at least one token).
+verification commits at least one token). Loop halting: per sequence, the
+relative change is ||h_cur - h_prev||_2 / ||h_prev||_2 over all its positions and
+hidden units (0/0 counts as no change); the loop halts after iteration k
+(1-based) when that change is below epsilon or k has reached the budget.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 things other than itself (library routines for special cases, closed forms,
@@ -379,6 +386,28 @@ def spec_accept(draft, first_choice, pass_argmax, S: int):
             n_commit[b] = S
             next_choice[b] = int(pa[b * S + S - 1])
     return {"tokens": tokens, "n_commit": n_commit, "next_choice": next_choice}
+
+
+# ----------------------------------------------------------------------------------------------
+# adaptive loop halting
+# ----------------------------------------------------------------------------------------------
+def loop_halt(h_prev, h_cur, eps: float, iteration: int, max_iter: int):
+    """Relative hidden-state change of every sequence between two consecutive loop iterations
+    and the halting decision after 1-based iteration ``iteration``.
+
+    h_prev, h_cur [B, ...] float64. rel[b] = ||h_cur[b] - h_prev[b]||_2 / ||h_prev[b]||_2 (both
+    zero -> 0; h_prev zero, h_cur not -> inf). halt[b] = rel[b] < eps (eps promoted from float32)
+    or iteration >= max_iter. Returns (rel [B] float64, halt [B] uint8)."""
+    B = h_prev.shape[0]
+    dp = np.asarray(h_prev, np.float64).reshape(B, -1)
+    dc = np.asarray(h_cur, np.float64).reshape(B, -1)
+    num = np.sqrt(((dc - dp) ** 2).sum(axis=1))
+    den = np.sqrt((dp ** 2).sum(axis=1))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(num == 0, 0.0, num / den)
+    e = float(np.float32(eps))
+    halt = ((rel < e) | (iteration >= max_iter)).astype(np.uint8)
+    return rel, halt
 
 
 def denoise_block(T: int, t0: int, B: int, S: int, mask0, tokens0, step_inputs: Callable,

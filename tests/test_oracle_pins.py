@@ -533,11 +533,51 @@ def test_spec_accept_is_lossless_against_ar_decoding():
     assert out[:3 + N] == ar[:3 + N]
 
 
+# -------------------------------------------------------------------------------- loop halting
+def test_loop_halt_closed_forms_and_library_norm():
+    rng = np.random.default_rng(31)
+    hp = rng.standard_normal((4, 7, 16))
+    a = np.array([0.5, -0.01, 0.0, 2.0])
+    hc = hp * (1 + a)[:, None, None]                         # scaled copy: rel = |a|
+    rel, halt = O.loop_halt(hp, hc, 0.05, 3, 10)
+    np.testing.assert_allclose(rel, np.abs(a), rtol=1e-12, atol=1e-15)
+    np.testing.assert_array_equal(halt, [0, 1, 1, 0])
+    d = rng.standard_normal((4, 7, 16))
+    hc2 = hp + d
+    rel2, _ = O.loop_halt(hp, hc2, 0.05, 3, 10)
+    ref = np.linalg.norm(d.reshape(4, -1), axis=1) / np.linalg.norm(hp.reshape(4, -1), axis=1)
+    np.testing.assert_allclose(rel2, ref, rtol=1e-12)
+    # the change is per sequence: perturbing one sequence moves only its value
+    hc3 = hc2.copy()
+    hc3[2] += 1.0
+    rel3, _ = O.loop_halt(hp, hc3, 0.05, 3, 10)
+    np.testing.assert_array_equal(rel3[[0, 1, 3]], rel2[[0, 1, 3]])
+    assert rel3[2] != rel2[2]
+
+
+def test_loop_halt_budget_and_degenerate_states():
+    hp = np.zeros((3, 5))
+    hc = np.zeros((3, 5))
+    hc[1, 0] = 1.0
+    hp[2] = 1.0
+    hc[2] = 1.0
+    rel, halt = O.loop_halt(hp, hc, 1e-3, 1, 4)
+    assert rel[0] == 0 and np.isinf(rel[1]) and rel[2] == 0
+    np.testing.assert_array_equal(halt, [1, 0, 1])
+    _, halt = O.loop_halt(hp, hc, 1e-3, 4, 4)                 # budget reached: every sequence halts
+    np.testing.assert_array_equal(halt, [1, 1, 1])
+    # strict comparison at a float32 epsilon
+    hp = np.ones((1, 4))
+    hc = hp * (1 + 0.25)
+    _, halt = O.loop_halt(hp, hc, 0.25, 1, 9)
+    assert halt[0] == 0
+
+
 def test_planted_mistakes_are_caught(monkeypatch):
     """Plant plausible slips in the oracle (on the CPU) and check that some pin fails."""
     orig = {k: getattr(O, k) for k in ("kv_head_of", "default_scale", "vocab_reduce", "keys_values",
                                        "softmax_attention", "merge_partials", "commit", "causal_visible",
-                                       "kv_append", "spec_accept")}
+                                       "kv_append", "spec_accept", "loop_halt")}
 
     def check(name, bad, pins):
         monkeypatch.setattr(O, name, bad)
@@ -616,3 +656,13 @@ def test_planted_mistakes_are_caught(monkeypatch):
         shifted = np.concatenate([pa[:, 1:], pa[:, -1:]], axis=1).reshape(-1)
         return orig["spec_accept"](draft, first_choice, shifted, S)
     check("spec_accept", unshifted, [(test_spec_accept_is_lossless_against_ar_decoding,)])
+
+    def halt_le(h_prev, h_cur, eps, iteration, max_iter):
+        rel, halt = orig["loop_halt"](h_prev, h_cur, eps, iteration, max_iter)
+        return rel, (halt | (rel <= float(np.float32(eps)))).astype(np.uint8)
+    check("loop_halt", halt_le, [(test_loop_halt_budget_and_degenerate_states,)])
+
+    def halt_squared(h_prev, h_cur, eps, iteration, max_iter):
+        rel, halt = orig["loop_halt"](h_prev, h_cur, eps, iteration, max_iter)
+        return rel ** 2, halt
+    check("loop_halt", halt_squared, [(test_loop_halt_closed_forms_and_library_norm,)])
