@@ -101,7 +101,8 @@ def row_figures(args, w, bd, torch, dev, recs, steps_used, commits, mask0, lens,
     written), vocab_reduce (the masked rows' logits), commit (latency only). Rows after the step,
     each timed on its own with the same trace (5 launches, first dropped): the context tower's
     causal pass over the block (bd_attn_step, causal), the append of the block to a cache
-    (bd_kv_append), the self-speculation check of a drafted block (bd_spec_verify)."""
+    (bd_kv_append), the self-speculation check of a drafted block (bd_spec_verify), and adaptive
+    loop halting (bd_loop_halt) on two hidden states of 32 x 1024 positions x 4096 units, bf16."""
     per = {}
     for name, ms in recs:
         per.setdefault(name, []).append(ms)
@@ -177,6 +178,23 @@ def row_figures(args, w, bd, torch, dev, recs, steps_used, commits, mask0, lens,
     tr.close()
     spec = [a + b for a, b in zip(sv.get("vocab_reduce", [])[1:], sv.get("spec_accept", [])[1:])]
     rows["spec_verify"] = fig(spec, w.B * w.S * w.V * lg_bytes)
+    hb, hn = 32, 1024 * 4096
+    g = torch.Generator(device=dev)
+    g.manual_seed(20261203)
+    h_prev = torch.randn((hb, hn), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    h_cur = (h_prev.float() + 1e-2 * torch.randn((hb, hn), generator=g, device=dev)).to(torch.bfloat16)
+    ws_h = torch.empty(bd.loop_halt_workspace_bytes(bd.halt_desc(hb, hn)), dtype=torch.uint8, device=dev)
+    tr = bd.Trace(capacity=64)
+    with tr:
+        for _ in range(5):
+            bd.loop_halt(h_prev, h_cur, 2, 1e-3, 12, workspace=ws_h)
+    lh = {}
+    for name, ms in tr.records():
+        lh.setdefault(name, []).append(ms)
+    tr.close()
+    halt = [a + b for a, b in zip(lh.get("halt_reduce", [])[1:], lh.get("halt_final", [])[1:])]
+    rows["loop_halt"] = fig(halt, 2 * hb * hn * 2)
+    del h_prev, h_cur
     torch.cuda.synchronize()
     return rows
 

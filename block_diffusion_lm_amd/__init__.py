@@ -7,6 +7,10 @@ no CPU or PyTorch fallback: a missing library raises.
     attn_step(q, k_blk, v_blk, k_cache, v_cache, prefix_len, ...)  -> (out, lse)
     confidence_unmask(logits, mask, tokens, block_len, gamma, ...)  -> dict
     denoise_block(get_qkv, get_logits, k_cache, v_cache, prefix_len, mask, tokens, T, ...) -> dict
+    attn_step(..., causal=True)                     context-tower pass over a committed block
+    kv_append(k_new, v_new, k_cache, v_cache, prefix_len, ...)  prefix-cache append
+    spec_verify(logits, draft, first_choice, block_len, ...)     self-speculation acceptance
+    loop_halt(h_prev, h_cur, iteration, eps, max_iter, ...)      adaptive loop halting
 """
 from __future__ import annotations
 
@@ -14,10 +18,11 @@ import ctypes
 from typing import Callable, Optional
 
 from . import _lib
-from ._lib import AttnDesc, BdError, StepHooks, UnmaskDesc  # noqa: F401
+from ._lib import AttnDesc, BdError, HaltDesc, StepHooks, UnmaskDesc  # noqa: F401
 
 __all__ = ["attn_step", "confidence_unmask", "denoise_block", "attn_desc", "unmask_desc", "Trace", "BdError",
-           "attn_workspace_bytes", "unmask_workspace_bytes", "denoise_workspace_bytes", "version"]
+           "attn_workspace_bytes", "unmask_workspace_bytes", "denoise_workspace_bytes", "version", "kv_append",
+           "spec_verify", "loop_halt", "halt_desc", "loop_halt_workspace_bytes"]
 
 
 def _torch():
@@ -166,6 +171,41 @@ def spec_verify(logits, draft, first_choice, block_len, vocab=None, tokens=None,
                                 _ptr(n_commit), _ptr(next_choice), _ptr(ws), ws.numel() if ws is not None else 0,
                                 _stream(stream)), "bd_spec_verify")
     return {"tokens": tokens, "n_commit": n_commit, "next_choice": next_choice}
+
+
+def halt_desc(B, n_per_seq, bf16=True, eps=1e-3, max_iter=8) -> HaltDesc:
+    return HaltDesc(B, n_per_seq, _lib.BD_BF16 if bf16 else _lib.BD_F32, eps, max_iter)
+
+
+def loop_halt_workspace_bytes(desc: HaltDesc) -> int:
+    return _lib.load().bd_loop_halt_workspace_bytes(ctypes.byref(desc))
+
+
+def loop_halt(h_prev, h_cur, iteration, eps, max_iter, rel=None, halt=None, want_rel=True, workspace=None,
+              stream=None):
+    """bd_loop_halt on torch tensors: h_prev / h_cur [B, ...] (bf16 or float32, same shape) are the
+    hidden states after loop iterations iteration-1 and iteration. Returns dict(rel [B] float32 or
+    None, halt [B] uint8)."""
+    torch = _torch()
+    L = _lib.load()
+    if h_prev.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("hidden states must be bfloat16 or float32")
+    _dev_tensor(h_prev, "h_prev")
+    _dev_tensor(h_cur, "h_cur", h_prev.dtype)
+    if h_cur.shape != h_prev.shape or h_prev.dim() < 1:
+        raise ValueError("h_prev / h_cur must have the same shape [B, ...]")
+    B = h_prev.shape[0]
+    n = h_prev.numel() // B if B else 0
+    desc = halt_desc(B, n, h_prev.dtype == torch.bfloat16, eps, max_iter)
+    dev = h_prev.device
+    if want_rel and rel is None:
+        rel = torch.empty(B, dtype=torch.float32, device=dev)
+    halt = torch.empty(B, dtype=torch.uint8, device=dev) if halt is None else halt
+    nbytes = L.bd_loop_halt_workspace_bytes(ctypes.byref(desc))
+    ws = _workspace(nbytes, dev, workspace)
+    _lib.check(L.bd_loop_halt(ctypes.byref(desc), _ptr(h_prev), _ptr(h_cur), int(iteration), _ptr(rel), _ptr(halt),
+                              _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)), "bd_loop_halt")
+    return {"rel": rel, "halt": halt}
 
 
 def confidence_unmask(logits, mask, tokens, block_len, gamma, vocab=None, min_commit=True, commit_all=False,

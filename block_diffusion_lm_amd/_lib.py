@@ -40,6 +40,16 @@ class UnmaskDesc(ctypes.Structure):
     ]
 
 
+class HaltDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_per_seq", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("max_iter", ctypes.c_int32),
+    ]
+
+
 GET_QKV = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                            ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                            ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p)
@@ -61,7 +71,7 @@ EXPORTS = [
     "bd_attn_workspace_bytes", "bd_attn_step", "bd_unmask_workspace_bytes", "bd_confidence_unmask",
     "bd_denoise_workspace_bytes", "bd_denoise_block", "bd_last_error", "bd_trace_create", "bd_trace_destroy",
     "bd_trace_attach", "bd_trace_clear", "bd_trace_count", "bd_trace_get", "bd_version", "bd_table_hooks",
-    "bd_kv_append", "bd_spec_verify",
+    "bd_kv_append", "bd_spec_verify", "bd_loop_halt_workspace_bytes", "bd_loop_halt",
 ]
 
 _lib = None
@@ -97,6 +107,10 @@ def load() -> ctypes.CDLL:
     L.bd_kv_append.restype = ctypes.c_int
     L.bd_spec_verify.argtypes = [P(UnmaskDesc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.bd_spec_verify.restype = ctypes.c_int
+    L.bd_loop_halt_workspace_bytes.argtypes = [P(HaltDesc)]
+    L.bd_loop_halt_workspace_bytes.restype = sz
+    L.bd_loop_halt.argtypes = [P(HaltDesc), vp, vp, i32, vp, vp, vp, sz, vp]
+    L.bd_loop_halt.restype = ctypes.c_int
     L.bd_table_hooks.argtypes = [P(StepTable), P(StepHooks)]
     L.bd_table_hooks.restype = ctypes.c_int
     L.bd_last_error.argtypes = []

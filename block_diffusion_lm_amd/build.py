@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libbd.so")
 
-SOURCES = ["bd_api.cpp", "bd_attn.hip", "bd_unmask.hip", "bd_cache.hip"]
+SOURCES = ["bd_api.cpp", "bd_attn.hip", "bd_unmask.hip", "bd_cache.hip", "bd_halt.hip"]
 
 # Packed fp32 vector instructions are disabled for every device compile (they are generated
 # automatically from scalar float code by -O3).

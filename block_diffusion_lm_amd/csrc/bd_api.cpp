@@ -272,6 +272,34 @@ bd_status check_ws(void* ws, size_t have, size_t need) {
   return BD_OK;
 }
 
+// ------------------------------------------------------------------------------------------
+// adaptive loop halting
+// ------------------------------------------------------------------------------------------
+bd_status check_halt_desc(const bd_halt_desc* d) {
+  if (!d) return fail(BD_EINVAL, "halting descriptor is NULL");
+  if (d->batch < 1) return fail(BD_EINVAL, "batch must be >= 1");
+  if (d->n_per_seq < 1) return fail(BD_EINVAL, "n_per_seq must be >= 1");
+  if (d->dtype != BD_BF16 && d->dtype != BD_F32) return fail(BD_EINVAL, "dtype must be BD_BF16 or BD_F32");
+  const int elt = d->dtype == BD_BF16 ? 2 : 4;
+  if ((d->n_per_seq * elt) % 16 != 0) return fail(BD_EINVAL, "n_per_seq * element size must be a multiple of 16 bytes");
+  if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return fail(BD_EINVAL, "eps must be finite and >= 0");
+  if (d->max_iter < 1) return fail(BD_EINVAL, "max_iter must be >= 1");
+  return BD_OK;
+}
+
+void plan_halt(const bd_halt_desc* d, int* nslice, int64_t* slice, size_t* bytes) {
+  // ~2048 workgroups of 256 threads, slices of >= 16384 values
+  int64_t ns = (2048 + d->batch - 1) / d->batch;
+  const int64_t cap = (d->n_per_seq + 16383) / 16384;
+  if (ns > cap) ns = cap;
+  if (ns < 1) ns = 1;
+  int64_t sl = (d->n_per_seq + ns - 1) / ns;
+  sl = (sl + 7) / 8 * 8;
+  *slice = sl;
+  *nslice = (int)((d->n_per_seq + sl - 1) / sl);
+  *bytes = align_up((size_t)d->batch * *nslice * 2 * sizeof(float), 256);
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,6 +419,46 @@ bd_status bd_spec_verify(const bd_unmask_desc* desc, const void* logits, const i
   st = traced("vocab_reduce", s, [&](const bd::Launch& l) { return bd::launch_vocab_reduce(a, l); });
   if (st != BD_OK) return st;
   return traced("spec_accept", s, [&](const bd::Launch& l) { return bd::launch_spec_accept(a, l); });
+}
+
+size_t bd_loop_halt_workspace_bytes(const bd_halt_desc* desc) {
+  if (check_halt_desc(desc) != BD_OK) return 0;
+  int ns;
+  int64_t sl;
+  size_t bytes;
+  plan_halt(desc, &ns, &sl, &bytes);
+  return bytes;
+}
+
+bd_status bd_loop_halt(const bd_halt_desc* desc, const void* h_prev, const void* h_cur, int32_t iteration,
+                       float* rel, uint8_t* halt, void* workspace, size_t workspace_bytes, void* stream) {
+  bd_status st = check_halt_desc(desc);
+  if (st != BD_OK) return st;
+  if (!h_prev || !h_cur || !aligned(h_prev, 16) || !aligned(h_cur, 16))
+    return fail(BD_EINVAL, "h_prev / h_cur must be non-NULL and 16-byte aligned");
+  if (!halt) return fail(BD_EINVAL, "halt is NULL");
+  if (rel && !aligned(rel, 4)) return fail(BD_EINVAL, "rel is not 4-byte aligned");
+  if (iteration < 1) return fail(BD_EINVAL, "iteration must be >= 1 (1-based)");
+  bd::HaltArgs a{};
+  size_t need;
+  plan_halt(desc, &a.nslice, &a.slice, &need);
+  st = check_ws(workspace, workspace_bytes, need);
+  if (st != BD_OK) return st;
+  a.h_prev = h_prev;
+  a.h_cur = h_cur;
+  a.is_bf16 = desc->dtype == BD_BF16;
+  a.B = desc->batch;
+  a.n = desc->n_per_seq;
+  a.part = static_cast<float*>(workspace);
+  a.eps = desc->eps;
+  a.iteration = iteration;
+  a.max_iter = desc->max_iter;
+  a.rel = rel;
+  a.halt = halt;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = traced("halt_reduce", s, [&](const bd::Launch& l) { return bd::launch_halt_reduce(a, l); });
+  if (st != BD_OK) return st;
+  return traced("halt_final", s, [&](const bd::Launch& l) { return bd::launch_halt_final(a, l); });
 }
 
 size_t bd_denoise_workspace_bytes(const bd_attn_desc* attn, const bd_unmask_desc* unmask) {

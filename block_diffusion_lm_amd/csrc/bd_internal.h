@@ -130,6 +130,27 @@ struct AppendArgs {
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, const Launch& l);
+
+// ---------------------------------------------------------------------------------------------
+// adaptive loop halting
+// ---------------------------------------------------------------------------------------------
+struct HaltArgs {
+  const void* h_prev;      // [B, n]
+  const void* h_cur;
+  int is_bf16;
+  int B;
+  int64_t n;               // values per sequence
+  int nslice;              // slices per sequence
+  int64_t slice;           // values per slice (multiple of 8)
+  float* part;             // [B][nslice][2]: sum (cur - prev)^2, sum prev^2
+  float eps;
+  int iteration, max_iter;
+  float* rel;              // [B] or nullptr
+  uint8_t* halt;           // [B]
+};
+
+hipError_t launch_halt_reduce(const HaltArgs& a, const Launch& l);
+hipError_t launch_halt_final(const HaltArgs& a, const Launch& l);
 hipError_t launch_len_advance(const AppendArgs& a, const Launch& l);
 
 }  // namespace bd

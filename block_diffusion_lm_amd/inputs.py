@@ -35,6 +35,7 @@ SEED_BASE = 20261203
 TENSOR_IDS = {
     "q": 0, "k_blk": 1, "v_blk": 2, "k_cache": 3, "v_cache": 4,
     "logits": 5, "mask": 6, "peaks": 7, "lens": 8, "ties": 9,
+    "h_prev": 10, "h_delta": 11,
 }
 
 
@@ -247,3 +248,23 @@ def small_workload(name: str = "small", B: int = 2, Hq: int = 8, Hkv: int = 2, D
     """Ad-hoc small workloads for parity sweeps (shapes spanning several tiles and a ragged tail)."""
     return Workload(name, wid, B, Hq, Hkv, D, S, prefix_len, V, logits_dtype, sigma, gamma,
                     mask_rule, peaks, ties, T)
+
+
+def loop_states(wid: int, B: int, n: int, scales, bf16: bool = True, zero_prev=(), same=()):
+    """Hidden states of a looped mid-block after two consecutive iterations, [B, n] each.
+
+    h_prev ~ N(0, 1); h_cur = h_prev + scales[b] * N(0, 1), drawn in float32 and then rounded
+    to bf16 (uint16 bits) when ``bf16``. Sequences listed in ``zero_prev`` get h_prev = 0;
+    those in ``same`` get h_cur = h_prev (no change). No hidden size is given for the looped
+    model, so n (positions x hidden units) is the caller's choice."""
+    x = rng(wid, "h_prev").standard_normal(size=(B, n), dtype=np.float32)
+    y = rng(wid, "h_delta").standard_normal(size=(B, n), dtype=np.float32)
+    y *= np.asarray(scales, np.float32).reshape(B, 1)
+    y += x
+    for b in zero_prev:
+        x[b] = 0
+    for b in same:
+        y[b] = x[b]
+    if bf16:
+        return f32_to_bf16_bits(x).reshape(B, n), f32_to_bf16_bits(y).reshape(B, n)
+    return x, y

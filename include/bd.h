@@ -28,6 +28,9 @@
  *  - Nemotron-Labs Diffusion page, decoding modes (self-speculation,
  *    LinearSpec): a block drafted bidirectionally is checked causally and its
  *    matching prefix commits (bd_spec_verify).
+ *  - Technical summary: LoopMDM, §Adaptive inference: the looped mid-block
+ *    stops once the relative hidden-state change between iterations falls
+ *    below epsilon or the iteration budget is spent (bd_loop_halt).
  *
  * Conventions (every entry point):
  *  - Pointers are DEVICE pointers unless marked (host). The caller owns every
@@ -196,6 +199,31 @@ bd_status bd_confidence_unmask(const bd_unmask_desc* desc, const void* logits,
 bd_status bd_spec_verify(const bd_unmask_desc* desc, const void* logits, const int32_t* draft,
                          const int32_t* first_choice, int32_t* tokens, int32_t* n_commit,
                          int32_t* next_choice, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Adaptive loop halting (LoopMDM)
+ *
+ * For every sequence b, with h_prev / h_cur its hidden state after loop iterations k-1 and k
+ * (n_per_seq values each, all positions and hidden units):
+ *   rel[b]  = ||h_cur[b] - h_prev[b]||_2 / ||h_prev[b]||_2   (0 when both norms are 0; +inf when
+ *             only h_prev's is), sums of squares in float32, in a fixed order;
+ *   halt[b] = rel[b] < eps (strict) or iteration >= max_iter  (iteration is 1-based: k).
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;            /* B >= 1 */
+  int64_t n_per_seq;        /* values per sequence (positions x hidden units), >= 1 */
+  bd_dtype dtype;           /* BD_BF16 or BD_F32 */
+  float eps;                /* >= 0, finite */
+  int32_t max_iter;         /* >= 1 */
+} bd_halt_desc;
+
+/* Workspace bytes bd_loop_halt needs (0 on an invalid descriptor). */
+size_t bd_loop_halt_workspace_bytes(const bd_halt_desc* desc);
+
+/* h_prev, h_cur: [B, n_per_seq] in desc.dtype (read only, rows contiguous, 16-byte aligned);
+ * iteration: k >= 1; rel: float32 [B] or NULL; halt: uint8 [B] (written). */
+bd_status bd_loop_halt(const bd_halt_desc* desc, const void* h_prev, const void* h_cur, int32_t iteration,
+                       float* rel, uint8_t* halt, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * The T-step block loop (Algorithm 1's inner loop)

@@ -198,3 +198,36 @@ def test_spec_verify_validation(L):
     assert L.bd_spec_verify(ctypes.byref(d), *([p] * 6), p, nb - 1, None) == _lib.BD_EWORKSPACE
     d.vocab = 0
     assert L.bd_spec_verify(ctypes.byref(d), *([p] * 6), p, nb, None) == _lib.BD_EINVAL
+
+
+def good_halt():
+    return _lib.HaltDesc(4, 4096, _lib.BD_BF16, 1e-3, 8)
+
+
+@pytest.mark.parametrize("field,value", [("batch", 0), ("n_per_seq", 0), ("n_per_seq", 4100), ("dtype", 7),
+                                         ("eps", -1.0), ("eps", math.inf), ("eps", math.nan), ("max_iter", 0)])
+def test_halt_descriptor_validation(L, field, value):
+    d = good_halt()
+    assert L.bd_loop_halt_workspace_bytes(ctypes.byref(d)) > 0
+    setattr(d, field, value)
+    assert L.bd_loop_halt_workspace_bytes(ctypes.byref(d)) == 0
+    p = ctypes.c_void_p(4096)
+    assert L.bd_loop_halt(ctypes.byref(d), p, p, 1, p, p, p, 1 << 20, None) == _lib.BD_EINVAL
+
+
+def test_halt_pointer_validation(L):
+    d = good_halt()
+    nb = L.bd_loop_halt_workspace_bytes(ctypes.byref(d))
+    assert nb % 256 == 0
+    p = ctypes.c_void_p(4096)
+    odd = ctypes.c_void_p(4104)
+    assert L.bd_loop_halt(ctypes.byref(d), None, p, 1, p, p, p, nb, None) == _lib.BD_EINVAL
+    assert L.bd_loop_halt(ctypes.byref(d), p, odd, 1, p, p, p, nb, None) == _lib.BD_EINVAL
+    assert L.bd_loop_halt(ctypes.byref(d), p, p, 1, p, None, p, nb, None) == _lib.BD_EINVAL
+    assert L.bd_loop_halt(ctypes.byref(d), p, p, 1, ctypes.c_void_p(4098), p, p, nb, None) == _lib.BD_EINVAL
+    assert L.bd_loop_halt(ctypes.byref(d), p, p, 0, p, p, p, nb, None) == _lib.BD_EINVAL
+    assert L.bd_loop_halt(ctypes.byref(d), p, p, 1, p, p, p, nb - 1, None) == _lib.BD_EWORKSPACE
+    assert L.bd_loop_halt(ctypes.byref(d), p, p, 1, p, p, None, nb, None) == _lib.BD_EINVAL
+    d.dtype = _lib.BD_F32
+    d.n_per_seq = 4
+    assert L.bd_loop_halt_workspace_bytes(ctypes.byref(d)) > 0
