@@ -12,9 +12,10 @@
 // tiles of 64 keys. Tiles are copied HBM -> LDS by LDS DMA (buffer/global loads with the lds
 // modifier, 16 bytes a lane), so the copy takes no registers and, for tiles inside the cached
 // prefix, no vector ALU work, into a ring of stages several tiles deep; one barrier per tile
-// publishes a landed tile and frees a consumed stage. Within a wave the 32-key blocks are
-// software-pipelined: the QK product of the next block is in flight while the current block's
-// softmax runs.
+// publishes a landed tile and frees a consumed stage. In eight-wave workgroups four waves issue
+// the copies. Within a wave the 32-key blocks are software-pipelined: the QK product of the next
+// block is in flight while the current block's exponentials run, and the P V product of the
+// current block while the next block's row maxima run.
 //
 // The host plans chunks for the whole batch; when only some sequences are still active (the
 // denoise loop retires sequences as their blocks complete) the kernels re-plan on the device:
@@ -28,8 +29,8 @@
 // The output is also accumulated transposed, O^T += V^T P^T (A = V^T, B = P^T), whose B operand
 // is exactly 8 consecutive accumulator registers of S^T converted to bf16. V stays row-major in
 // LDS; its A operand is gathered with transposing LDS reads (ds_read_b64_tr_b16) whose per-lane
-// key addresses follow the key order of those accumulator registers. K rows carry one pad chunk
-// and V rows a 64-byte block swizzle, so neither operand read has bank conflicts.
+// key addresses follow the key order of those accumulator registers. The 16-byte chunks of K rows
+// and the 64-byte blocks of V rows are swizzled by row, so neither operand read has bank conflicts.
 //
 // Softmax: online (running max m, running sum l) in log2 units, exp2 in float32, P rounded to
 // bf16 for the P V product; l sums the same bf16-rounded P (v_dot2), so numerator and
@@ -114,7 +115,7 @@ template <int D>
 struct Geo {
   static constexpr int KT = kAttnKeyTile;           // keys per LDS tile
   static constexpr int KB = KT / 32;                // 32-key MFMA blocks per tile
-  static constexpr int KROW = D * 2 + 16;          // bytes per key row of the K tile: D values + a pad chunk
+  static constexpr int KROW = D * 2;                // bytes per key row of the K tile (16-byte chunks swizzled)
   static constexpr int VROW = D * 2;                // bytes per key row of the V tile (64-byte blocks swizzled)
   static constexpr int KBYTES = KT * KROW;
   static constexpr int VBYTES = KT * VROW;
@@ -229,10 +230,12 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
   constexpr int NT = NW * 64;
   constexpr int NSTAGE = attn_stages(D, NW * RB);
   constexpr int JV = G::J - G::JK;
-  constexpr int SK = (G::JK + NW - 1) / NW;       // K / V DMA instructions a wave issues per tile (at most)
-  constexpr int SV = (JV + NW - 1) / NW;
-  constexpr int NMIN = G::JK / NW + JV / NW;       // ... in all (at least): the waits count on this many
-  static_assert(NMIN * 3 < 64 && NSTAGE <= 4, "vmcnt range");
+  constexpr int NWD = NW >= 8 ? NW / 2 : NW;      // waves that issue the tile copies
+  constexpr int NK = G::JK / NWD;                  // K / V DMA instructions such a wave issues per tile
+  constexpr int NV = JV / NWD;
+  constexpr int NMIN = NK + NV;                    // the waits count on this many per tile
+  static_assert(NK * NWD == G::JK && NV * NWD == JV && NWD % 2 == 0, "copies split evenly over the copying waves");
+  static_assert(NMIN * 3 < 64 && NSTAGE <= 5, "vmcnt range");
 
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * G::STAGE];
 
@@ -293,42 +296,45 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
 
   // ---- tile filling by LDS DMA. A stage is JK + JV wave instructions of 1 KB (64 lanes x 16 B):
   // K instruction j writes stage bytes [1024 j, 1024 j + 1024), V instruction j the same range of
-  // the V region; wave w issues instructions w, w + NW, ... of each. koff / voff: byte offset,
-  // from the tile's first key row, of the 16 source bytes this lane moves in each of its
-  // instructions -- K rows are copied with a pad chunk (a copy of the row's last chunk), V rows
-  // with their 64-byte blocks swizzled.
+  // the V region; copying wave w issues instructions w, w + NWD, ... of each.
   // buffer resources over this (sequence, KV head)'s cached rows (buffer offsets are 32-bit)
   const __amdgpu_buffer_rsrc_t rsrc_k = raw_rsrc(kc, (uint64_t)a.lcap * D * 2);
   const __amdgpu_buffer_rsrc_t rsrc_v = raw_rsrc(vc, (uint64_t)a.lcap * D * 2);
-  uint32_t koff[SK], voff[SV];
-#pragma unroll
-  for (int i = 0; i < SK; ++i) {
-    const int p = (wave + NW * i) * 1024 + lane * 16;
-    const int row = p / G::KROW;
-    const int ch = min((p % G::KROW) / 16, D / 8 - 1);
-    koff[i] = (uint32_t)(row * D * 2 + ch * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < SV; ++i) {
-    const int p = (wave + NW * i) * 1024 + lane * 16;
-    const int row = p / G::VROW;
-    const int blk = (p % G::VROW) / 64;
-    voff[i] = (uint32_t)(row * G::VROW + ((blk ^ vswz<D>(row)) * 64) + (p % 64));
+  // Per-lane source offsets. K instruction j fills K rows r = 4j + lane / 16 (D = 128; 8j + lane / 8
+  // for D = 64) with their 16-byte chunks at swizzled positions: chunk c of row r sits at position
+  // c ^ (r & 7), so the K fragment reads below hit eight different bank groups. A lane's position
+  // is fixed by the DMA (lane order), so it fetches the chunk that belongs there; r & 7 depends on
+  // j only through j's parity, which is the copying wave's parity. V rows keep their 64-byte block
+  // swizzle, which does not depend on j at all. Instruction j adds 1024 j to both.
+  uint32_t kl, vl;
+  {
+    constexpr int LPR = D * 2 / 16;   // lanes per row (16-byte chunks per row)
+    const int r = (wave & 1) * (1024 / (D * 2)) + lane / LPR;   // row within the pair of instructions
+    const int pos = lane % LPR;
+    kl = (uint32_t)((lane / LPR) * D * 2 + 16 * (pos ^ (r & 7)));
+    const int vr = lane / LPR;
+    const int vp = lane * 16;
+    vl = (uint32_t)(vr * G::VROW + ((((vp % G::VROW) / 64) ^ vswz<D>(vr)) * 64) + (vp % 64));
   }
   // The tile at kt0 into stage `stage`. A tile that lies wholly inside the cached prefix and the
   // chunk (all but at most two per chunk) is one uniform base per tensor; otherwise sources are
   // per lane: cache rows, block rows past the prefix end, and rows past the chunk end repeating
   // its last key (finite data whose scores are masked).
   auto issue_tile = [&](int stage, int64_t kt0) {
+    if (wave >= NWD) return;
     char* dst = smem + stage * G::STAGE;
     if (kt0 + G::KT <= len && kt0 + G::KT <= k_end) {
       const uint32_t soff = (uint32_t)(kt0 * D * 2);
 #pragma unroll
-      for (int i = 0; i < SK; ++i)
-        if (wave + NW * i < G::JK) dma16_buf(rsrc_k, koff[i], soff, dst + (wave + NW * i) * 1024);
+      for (int i = 0; i < NK; ++i) {
+        const int j = wave + NWD * i;
+        dma16_buf(rsrc_k, kl, soff + 1024 * j, dst + 1024 * j);
+      }
 #pragma unroll
-      for (int i = 0; i < SV; ++i)
-        if (wave + NW * i < JV) dma16_buf(rsrc_v, voff[i], soff, dst + G::KBYTES + (wave + NW * i) * 1024);
+      for (int i = 0; i < NV; ++i) {
+        const int j = wave + NWD * i;
+        dma16_buf(rsrc_v, vl, soff + 1024 * j, dst + G::KBYTES + 1024 * j);
+      }
     } else {
       auto src_of = [&](uint32_t off, const uint16_t* cache, const uint16_t* blk) {
         const int64_t key = min(kt0 + (int64_t)(off / (D * 2)), k_end - 1);
@@ -336,17 +342,28 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
         return reinterpret_cast<const char*>(row) + off % (D * 2);
       };
 #pragma unroll
-      for (int i = 0; i < SK; ++i)
-        if (wave + NW * i < G::JK) dma16(src_of(koff[i], kc, kb0), dst + (wave + NW * i) * 1024);
+      for (int i = 0; i < NK; ++i) {
+        const int j = wave + NWD * i;
+        dma16(src_of(kl + 1024 * j, kc, kb0), dst + 1024 * j);
+      }
 #pragma unroll
-      for (int i = 0; i < SV; ++i)
-        if (wave + NW * i < JV) dma16(src_of(voff[i], vc, vb0), dst + G::KBYTES + (wave + NW * i) * 1024);
+      for (int i = 0; i < NV; ++i) {
+        const int j = wave + NWD * i;
+        dma16(src_of(vl + 1024 * j, vc, vb0), dst + G::KBYTES + 1024 * j);
+      }
     }
   };
 
   // ---- operand addresses inside a stage
   // K fragment (A of S^T = K Q^T): key kb*32 + lrow, dims 16 kstep + 8 half .. +7
-  const uint32_t k_lane = (uint32_t)(lrow * G::KROW + half * 16);
+  // K fragment kstep k reads chunk 2k + half of key lrow, stored at position (2k + half) ^ s with
+  // s = lrow & 7: byte 128 (k >> 2) + 32 ((k & 3) ^ (s >> 1)) + 16 (half ^ (s & 1)) of the row.
+  uint32_t k_lane[4];
+  {
+    const int sw = lrow & 7;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) k_lane[q] = (uint32_t)(lrow * G::KROW + 32 * (q ^ (sw >> 1)) + 16 * (half ^ (sw & 1)));
+  }
   // V^T fragment (A of O^T = V^T P^T) for 32-dim block db: two transposing reads, keys
   // 16e + 4 half + 0..3 and 16e + 8 + 4 half + 0..3 -- the key order of the P^T operand below.
   uint32_t v_lane[G::DB];
@@ -386,9 +403,10 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
   };
   // K fragments of block kb of the tile in stage st, and S^T = K Q^T from them
   auto load_k = [&](int st, int kb, bf16x8 (&kf)[G::KS]) {
-    const char* ks = smem + st * G::STAGE + k_lane + kb * 32 * G::KROW;
+    const char* ks = smem + st * G::STAGE + kb * 32 * G::KROW;
 #pragma unroll
-    for (int kstep = 0; kstep < G::KS; ++kstep) kf[kstep] = *reinterpret_cast<const bf16x8*>(ks + kstep * 32);
+    for (int kstep = 0; kstep < G::KS; ++kstep)
+      kf[kstep] = *reinterpret_cast<const bf16x8*>(ks + k_lane[kstep & 3] + 128 * (kstep >> 2));
   };
   auto qk = [&](const bf16x8 (&kf)[G::KS], f32x16 (&sacc)[RB]) {
 #pragma unroll
@@ -452,43 +470,41 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
       }
     }
   };
-  // P = exp2(s*sc - m) in bf16, row sums of the rounded P, O^T += V^T P^T
-  auto exp_pv = [&](const f32x16 (&sacc)[RB], const bf16x8 (&vf)[2][G::DB]) {
+  // P = exp2(s*sc - m) in bf16 for the two 16-key steps e, and the row sums of the rounded P
+  auto exp_p = [&](const f32x16 (&sacc)[RB], bf16x8 (&pf)[2][RB]) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      bf16x8 pf[RB];
+    for (int rb = 0; rb < RB; ++rb) {
+      // no visible key yet for this row (causal pass): every P is 0, not exp2(nan)
+      const float mneg = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
+      float ls = l_run[rb];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        // no visible key yet for this row (causal pass): every P is 0, not exp2(nan)
-        const float mneg = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
+      for (int e = 0; e < 2; ++e) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pf[rb][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[rb][8 * e + i], sc, mneg));
-        float ls = l_run[rb];
+        for (int i = 0; i < 8; ++i) pf[e][rb][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[rb][8 * e + i], sc, mneg));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bf16x2 p2 = {pf[rb][2 * i], pf[rb][2 * i + 1]};
+          const bf16x2 p2 = {pf[e][rb][2 * i], pf[e][rb][2 * i + 1]};
           ls = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, ls, false);
         }
-        l_run[rb] = ls;
       }
+      l_run[rb] = ls;
+    }
+  };
+  // O^T += V^T P^T
+  auto pv = [&](const bf16x8 (&vf)[2][G::DB], const bf16x8 (&pf)[2][RB]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma32(vf[e][db], pf[rb], o[rb][db]);
-    }
+        for (int rb = 0; rb < RB; ++rb) o[rb][db] = mfma32(vf[e][db], pf[e][rb], o[rb][db]);
+  };
+  // LDS addresses of the V^T reads of block kb of the tile in stage st
+  auto v_addr = [&](int st, int kb, uint32_t (&va)[G::DB]) {
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) va[db] = smem_lds + st * G::STAGE + G::KBYTES + kb * 32 * G::VROW + v_lane[db];
   };
 
-  // ---- software pipeline over 32-key blocks. Each block reads the K fragments of the next block
-  // first, then its own V^T operands (one LDS round trip for both), and issues the next block's
-  // QK product in the same straight-line region as its own row maxima, and its exponentials in
-  // the same region as its P V products, so one wave's MFMAs and VALU work can overlap. A QK
-  // product of a block that does not exist (past the last tile, or the odd half of a short last
-  // tile) reads stale but in-bounds LDS and is never used.
-  //
-  // Ring of NSTAGE >= 3 stages: tile t + 1 is published by a barrier between the two blocks of
-  // tile t, which also frees tile t - 1's stage for tile t + NSTAGE - 1 (NSTAGE - 2 tiles of DMA
-  // stay in flight). With 2 stages, tile t + 1 is published after tile t's odd block has read its
-  // V^T operands, freeing tile t's stage for tile t + 2.
   static_assert(G::KB == 2, "two 32-key blocks per tile");
   constexpr int AHEAD = NSTAGE >= 3 ? NSTAGE - 1 : NSTAGE;   // tiles issued before the loop
 #pragma unroll
@@ -496,31 +512,102 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
     if (s < ntiles) issue_tile(s, k_begin + (int64_t)s * G::KT);
   wait_tile(min(AHEAD - 1, ntiles - 1));
   f32x16 s_even[RB], s_odd[RB];   // S^T of the even and the odd block of a tile
-  if (wave_rows) {
+
+  // ---- full tiles (ring of NSTAGE >= 3 stages). A tile wholly inside the cached prefix and the
+  // chunk needs no key mask. Block j runs as two straight-line regions:
+  //   A: V^T reads of block j, the QK product of block j + 1 (K read in the previous B) and the
+  //      exponentials of block j -- MFMA and VALU work without dependences between them;
+  //   B: the P V product of block j, the K reads of block j + 2 and the row maxima of block j + 1.
+  // The rare rescale (a branch) follows B. Between A and B of the even block of tile t a barrier
+  // publishes tile t + 1 and frees tile t - 1's stage for tile t + NSTAGE - 1.
+  int t0 = 0;   // first tile of the general loop below
+  if constexpr (NSTAGE >= 3) {
+    const int64_t fe = min(len, k_end);
+    const int nfull = fe > k_begin ? (int)((fe - k_begin) / G::KT) : 0;
+    if (nfull > 0) {
+      f32x16 s_cur[RB];
+      bf16x8 kf[G::KS];
+      float mx[RB];
+      if (wave_rows) {
+        load_k(0, 0, kf);
+        qk(kf, s_cur);
+        row_max(s_cur, mx);
+        rescale(mx, true);
+        load_k(0, 1, kf);
+      }
+      // block j = 2t + kb of tile t; `last`: the odd block of the last full tile (no block j + 2)
+      auto block = [&](int t, int kb, bool last) {
+        const int st = t % NSTAGE;
+        bf16x8 vf[2][G::DB];
+        bf16x8 pf[2][RB];
+        f32x16 s_nxt[RB];
+        if (wave_rows) {
+          uint32_t va[G::DB];
+          v_addr(st, kb, va);
+          read_vt<D, 0>(va, vf);
+          qk(kf, s_nxt);
+          exp_p(s_cur, pf);
+        }
+        if (kb == 0) {
+          wait_tile(min(NSTAGE - 3, ntiles - 2 - t));
+          if (t + NSTAGE - 1 < ntiles) issue_tile((t + NSTAGE - 1) % NSTAGE, k_begin + (int64_t)(t + NSTAGE - 1) * G::KT);
+        }
+        if (wave_rows) {
+          pv(vf, pf);
+          if (!last) {
+            load_k((t + 1) % NSTAGE, kb, kf);
+            row_max(s_nxt, mx);
+            rescale(mx, true);
+          }
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) s_cur[rb] = s_nxt[rb];
+        }
+      };
+      for (int t = 0; t < nfull - 1; ++t) {
+        block(t, 0, false);
+        block(t, 1, false);
+      }
+      block(nfull - 1, 0, false);
+      block(nfull - 1, 1, true);
+      // s_cur holds the QK product of the first block after the full tiles (if any)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s_even[rb] = s_cur[rb];
+      t0 = nfull;
+    }
+  }
+  if (t0 == 0 && wave_rows) {
     bf16x8 kf[G::KS];
     load_k(0, 0, kf);
     qk(kf, s_even);
   }
 
-  for (int t = 0; t < ntiles; ++t) {
+  // ---- general loop (tiles at a chunk end or holding block keys; every tile when the ring has two
+  // stages). Each block reads the K fragments of the next block first, then its own V^T operands,
+  // and issues the next block's QK product in the same straight-line region as its own row maxima.
+  // A QK product of a block that does not exist (past the last tile, or the odd half of a short
+  // last tile) reads stale but in-bounds LDS and is never used. With 2 stages, tile t + 1 is
+  // published after tile t's odd block has read its V^T operands, freeing tile t's stage for tile
+  // t + 2.
+  for (int t = t0; t < ntiles; ++t) {
     const int st = t % NSTAGE;
     const int valid = (int)min((int64_t)G::KT, k_end - (k_begin + (int64_t)t * G::KT));   // keys of tile t
     const bool odd = valid > 32;                  // tile t has a second block
-    uint32_t vaddr[G::DB];
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db) vaddr[db] = smem_lds + st * G::STAGE + G::KBYTES + v_lane[db];
     bf16x8 vf[2][G::DB];
+    bf16x8 pf[2][RB];
     float mx[RB];
     // ---- even block
     if (wave_rows) {
       bf16x8 kf[G::KS];
       load_k(st, 1, kf);
-      read_vt<D, 0>(vaddr, vf);
+      uint32_t va[G::DB];
+      v_addr(st, 0, va);
+      read_vt<D, 0>(va, vf);
       mask_keys(s_even, k_begin + (int64_t)t * G::KT, min(valid, 32));
       qk(kf, s_odd);
       row_max(s_even, mx);
       rescale(mx, true);
-      exp_pv(s_even, vf);
+      exp_p(s_even, pf);
+      pv(vf, pf);
     }
     if constexpr (NSTAGE >= 3) {
       // publish tile t + 1; tile t - 1's stage is free (waves without rows take part too)
@@ -531,7 +618,9 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
     if (wave_rows) {
       bf16x8 kf[G::KS];
       if constexpr (NSTAGE >= 3) load_k((t + 1) % NSTAGE, 0, kf);
-      read_vt<D, 32 * G::VROW>(vaddr, vf);
+      uint32_t va[G::DB];
+      v_addr(st, 1, va);
+      read_vt<D, 0>(va, vf);
       mask_keys(s_odd, k_begin + (int64_t)t * G::KT + 32, max(valid - 32, 0));
       if constexpr (NSTAGE < 3) {
         wait_tile(min(NSTAGE - 2, ntiles - 2 - t));
@@ -541,7 +630,10 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
       qk(kf, s_even);
       row_max(s_odd, mx);
       rescale(mx, odd);
-      if (odd) exp_pv(s_odd, vf);
+      if (odd) {
+        exp_p(s_odd, pf);
+        pv(vf, pf);
+      }
     } else if constexpr (NSTAGE < 3) {
       wait_tile(min(NSTAGE - 2, ntiles - 2 - t));
       if (t + NSTAGE < ntiles) issue_tile(st, k_begin + (int64_t)(t + NSTAGE) * G::KT);

@@ -8,7 +8,7 @@
 // halt_reduce: one workgroup per (sequence, slice) streams its slice of both states once with
 // 16-byte loads (HBM-bound: 2 x n x element bytes per sequence) and keeps per-thread float32 sums
 // of (cur - prev)^2 and prev^2, combined in a fixed order (wave butterflies, then the four waves
-// in order). halt_final: one thread per sequence adds its slices in order and decides.
+// in order). halt_final: one wave per sequence adds its slices in a fixed order and decides.
 #include "bd_internal.h"
 
 namespace bd {
@@ -89,18 +89,26 @@ __global__ __launch_bounds__(256) void halt_reduce_kernel(HaltArgs a) {
   }
 }
 
+// One wave per sequence: lane j adds slices j, j + 64, ... in order, then a fixed butterfly.
 __global__ __launch_bounds__(64) void halt_final_kernel(HaltArgs a) {
-  const int b = blockIdx.x * 64 + threadIdx.x;
-  if (b >= a.B) return;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
   const float* pp = a.part + (int64_t)b * a.nslice * 2;
   float d2 = 0.f, p2 = 0.f;
-  for (int c = 0; c < a.nslice; ++c) {
+  for (int c = lane; c < a.nslice; c += 64) {
     d2 += pp[2 * c];
     p2 += pp[2 * c + 1];
   }
-  const float r = d2 == 0.f ? 0.f : sqrtf(d2) / sqrtf(p2);   // p2 == 0 < d2: +inf
-  if (a.rel) a.rel[b] = r;
-  a.halt[b] = (r < a.eps || a.iteration >= a.max_iter) ? 1 : 0;
+#pragma unroll
+  for (int msk = 32; msk > 0; msk >>= 1) {
+    d2 += __shfl_xor(d2, msk, 64);
+    p2 += __shfl_xor(p2, msk, 64);
+  }
+  if (lane == 0) {
+    const float r = d2 == 0.f ? 0.f : sqrtf(d2) / sqrtf(p2);   // p2 == 0 < d2: +inf
+    if (a.rel) a.rel[b] = r;
+    a.halt[b] = (r < a.eps || a.iteration >= a.max_iter) ? 1 : 0;
+  }
 }
 
 }  // namespace
@@ -110,7 +118,7 @@ hipError_t launch_halt_reduce(const HaltArgs& a, const Launch& l) {
 }
 
 hipError_t launch_halt_final(const HaltArgs& a, const Launch& l) {
-  return launch_kernel(halt_final_kernel, dim3((unsigned)((a.B + 63) / 64)), dim3(64), l, a);
+  return launch_kernel(halt_final_kernel, dim3((unsigned)a.B), dim3(64), l, a);
 }
 
 }  // namespace bd

@@ -28,9 +28,9 @@ hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, const Launch& l, Args.
 // ---------------------------------------------------------------------------------------------
 
 // LDS ring of the attention split kernel, shared by the kernel and the host planner: a stage holds
-// one tile of kAttnKeyTile keys (K rows with one 16-byte pad chunk each, then unpadded V rows).
+// one tile of kAttnKeyTile keys (K rows, then V rows; D values each, 16-byte chunks or 64-byte blocks swizzled).
 constexpr int kAttnKeyTile = 64;
-constexpr int attn_stage_bytes(int head_dim) { return kAttnKeyTile * (head_dim * 2 + 16) + kAttnKeyTile * head_dim * 2; }
+constexpr int attn_stage_bytes(int head_dim) { return 2 * kAttnKeyTile * head_dim * 2; }
 // stages in the ring: 256-row workgroups (one per CU) prefetch three tiles ahead; 128-row
 // workgroups (two per CU) one, except at head_dim 64 where four stages still fit twice.
 constexpr int attn_stages(int head_dim, int row_blocks) { return (row_blocks == 8 || head_dim == 64) ? 4 : 2; }
