@@ -686,127 +686,97 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
 }
 
 // Merge of the chunk partials of every (sequence, KV head, query row): with M = max_c m_c,
-//   O = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M),  LSE = (M + log2 sum_c l_c 2^(m_c - M)) ln 2,
-// chunks combined in index order.
+//   O = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M),  LSE = (M + log2 sum_c l_c 2^(m_c - M)) ln 2.
 //
-// Narrow form (few chunks): one thread per (row, 4 dims), the chunk loop unrolled so several
-// partial loads are in flight per thread.
-template <int D>
-__global__ __launch_bounds__(256) void attn_merge_narrow_kernel(AttnArgs a, int tile_rows) {
+// 256 threads = RW rows x CG chunk groups x (D/4 groups of 4 dims). Chunk group j takes chunks
+// j, j + CG, ... in index order, U at a time (all their loads in flight together), keeping a
+// running maximum: when a group of U raises it, the sums so far are scaled down first. The
+// chunk groups are then combined in index order through LDS, so the result does not depend on
+// scheduling. A chunk without a visible key (m = -inf, causal pass) contributes nothing.
+template <int D, int CG, int U>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int tile_rows) {
   constexpr int DG = D / 4;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.Hkv * a.rows * DG;
-  if (gid >= total) return;
-  const int dg = (int)(gid % DG);
-  const int64_t rowg = gid / DG;
-  const int r = (int)(rowg % a.rows);
-  const int pair = (int)(rowg / a.rows);
+  constexpr int RW = 256 / (DG * CG);
+  static_assert(RW * DG * CG == 256, "thread layout");
+  __shared__ float red_m[CG > 1 ? 256 : 1];
+  __shared__ float red_den[CG > 1 ? 256 : 1];
+  __shared__ f32x4 red_num[CG > 1 ? 256 : 1];
+  const int tid = threadIdx.x;
+  const int dg = tid % DG;
+  const int cg = (tid / DG) % CG;
+  const int rw = tid / (DG * CG);
+  const int64_t rowg = (int64_t)blockIdx.x * RW + rw;
+  const bool live = rowg < (int64_t)a.B * a.Hkv * a.rows;
+  const int r = live ? (int)(rowg % a.rows) : 0;
+  const int pair = live ? (int)(rowg / a.rows) : 0;
   const int b = pair / a.Hkv;
   const int g = pair % a.Hkv;
-  if (a.active && !a.active[b]) return;
+  const bool act = live && !(a.active && !a.active[b]);
   const int n_act = count_active(a.active, a.B);
   const ItemMap im = device_plan(a, n_act);
   if (im.nsplit == 1) return;   // the split kernel wrote the output itself
-  const int64_t pair_a = (int64_t)rank_active(a.active, b) * a.Hkv + g;
-  const int64_t nkeys = (int64_t)a.prefix_len[b] + a.S;
-  const int ns = (int)min((int64_t)im.nsplit, (nkeys + im.chunk - 1) / im.chunk);
-  const int rt = r / tile_rows;
-  const int rr = r - rt * tile_rows;
-  const int64_t pstride = (int64_t)a.row_tiles * tile_rows;     // partial rows between chunks
-  const int64_t p0 = ((pair_a * im.nsplit) * a.row_tiles + rt) * tile_rows + rr;
-  float M = -INFINITY;
-  for (int c = 0; c < ns; ++c) M = fmaxf(M, a.part_ml[(p0 + c * pstride) * 2]);
+  int ns = 0;
+  int64_t p0 = 0, pstride = 0;
+  if (act) {
+    const int64_t pair_a = (int64_t)rank_active(a.active, b) * a.Hkv + g;
+    const int64_t nkeys = (int64_t)a.prefix_len[b] + a.S;
+    ns = (int)min((int64_t)im.nsplit, (nkeys + im.chunk - 1) / im.chunk);
+    const int rt = r / tile_rows;
+    pstride = (int64_t)a.row_tiles * tile_rows;   // partial rows between chunks
+    p0 = ((pair_a * im.nsplit) * a.row_tiles + rt) * tile_rows + (r - rt * tile_rows);
+  }
+  float M = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  int c = 0;
-  for (; c + 4 <= ns; c += 4) {
-    f32x4 v[4];
-    float mm[4], ll[4];
+  for (int c0 = cg; c0 < ns; c0 += U * CG) {
+    float mm[U], ll[U];
+    f32x4 v[U];
+    // every slot loads (past the last chunk: the last chunk again, then ignored), so that all the
+    // loads of the group are issued before the first is used
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t pr = p0 + (c + j) * pstride;
-      mm[j] = a.part_ml[pr * 2];
-      ll[j] = a.part_ml[pr * 2 + 1];
+    for (int j = 0; j < U; ++j) {
+      const int c = min(c0 + j * CG, ns - 1);
+      const int64_t pr = p0 + c * pstride;
+      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
+      mm[j] = c0 + j * CG < ns ? ml.x : -INFINITY;
+      ll[j] = ml.y;
       v[j] = *reinterpret_cast<const f32x4*>(a.part_acc + pr * D + dg * 4);
     }
+    float gm = mm[0];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float w = __builtin_amdgcn_exp2f(mm[j] - M);
+    for (int j = 1; j < U; ++j) gm = fmaxf(gm, mm[j]);
+    if (gm > M) {
+      const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - gm);
+      den *= sc;
+      num *= sc;
+      M = gm;
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const float w = mm[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[j] - M);
       den += ll[j] * w;
       num += v[j] * w;
     }
   }
-  for (; c < ns; ++c) {
-    const int64_t pr = p0 + c * pstride;
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - M);
-    den += a.part_ml[pr * 2 + 1] * w;
-    num += *reinterpret_cast<const f32x4*>(a.part_acc + pr * D + dg * 4) * w;
-  }
-  const float inv = 1.0f / den;
-  const int s = r / a.group;
-  const int hq = g * a.group + (r - s * a.group);
-  bf16x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = (__bf16)(num[i] * inv);
-  *reinterpret_cast<bf16x4*>(a.out + (((int64_t)b * a.S + s) * a.Hq + hq) * D + dg * 4) = o;
-  if (a.lse && dg == 0) a.lse[((int64_t)b * a.Hq + hq) * a.S + s] = (M + log2f(den)) * kLn2;
-}
-
-// Wide form (many chunks): one workgroup per query row: 256 threads = (D/4 groups of 4 dims) x (256/(D/4) split groups);
-// split group j sums chunks j, j + SG, ... in order, then the groups are added in index order
-// through LDS, so the result does not depend on scheduling.
-template <int D>
-__global__ __launch_bounds__(256) void attn_merge_wide_kernel(AttnArgs a, int tile_rows) {
-  constexpr int DG = D / 4;
-  constexpr int SG = 256 / DG;
-  __shared__ float red_m[256];
-  __shared__ f32x4 red_num[256];
-  __shared__ float red_den[256];
-  const int tid = threadIdx.x;
-  const int64_t rowg = blockIdx.x;
-  const int r = (int)(rowg % a.rows);
-  const int pair = (int)(rowg / a.rows);
-  const int b = pair / a.Hkv;
-  const int g = pair % a.Hkv;
-  if (a.active && !a.active[b]) return;
-  const int n_act = count_active(a.active, a.B);
-  const ItemMap im = device_plan(a, n_act);
-  if (im.nsplit == 1) return;   // the split kernel wrote the output itself
-  const int64_t pair_a = (int64_t)rank_active(a.active, b) * a.Hkv + g;
-  const int64_t nkeys = (int64_t)a.prefix_len[b] + a.S;
-  const int ns = (int)min((int64_t)im.nsplit, (nkeys + im.chunk - 1) / im.chunk);
-  const int rt = r / tile_rows;
-  const int rr = r - rt * tile_rows;
-  const int64_t pstride = (int64_t)a.row_tiles * tile_rows;     // partial rows between chunks
-  const int64_t p0 = ((pair_a * im.nsplit) * a.row_tiles + rt) * tile_rows + rr;
-  // M = max over chunks
-  float mloc = -INFINITY;
-  for (int c = tid; c < ns; c += 256) mloc = fmaxf(mloc, a.part_ml[(p0 + c * pstride) * 2]);
-  red_m[tid] = mloc;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red_m[tid] = fmaxf(red_m[tid], red_m[tid + w]);
+  if constexpr (CG > 1) {
+    red_m[tid] = M;
+    red_den[tid] = den;
+    red_num[tid] = num;
     __syncthreads();
+    if (cg != 0) return;
+    const int base = rw * DG * CG + dg;
+#pragma unroll
+    for (int j = 1; j < CG; ++j) M = fmaxf(M, red_m[base + j * DG]);
+    den = 0.f;
+    num = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      const float mj = red_m[base + j * DG];
+      const float w = mj == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mj - M);
+      den += red_den[base + j * DG] * w;
+      num += red_num[base + j * DG] * w;
+    }
   }
-  const float M = red_m[0];
-  const int dg = tid % DG;
-  const int sg = tid / DG;
-  f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  for (int c = sg; c < ns; c += SG) {
-    const int64_t pr = p0 + c * pstride;
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - M);
-    den += a.part_ml[pr * 2 + 1] * w;
-    num += *reinterpret_cast<const f32x4*>(a.part_acc + pr * D + dg * 4) * w;
-  }
-  red_num[tid] = num;
-  red_den[tid] = den;
-  __syncthreads();
-  if (sg != 0) return;
-  for (int j = 1; j < SG; ++j) {
-    num += red_num[j * DG + dg];
-    den += red_den[j * DG + dg];
-  }
+  if (!act) return;
   const float inv = 1.0f / den;
   const int s = r / a.group;
   const int hq = g * a.group + (r - s * a.group);
@@ -836,15 +806,22 @@ hipError_t launch_attn_split(const AttnPlan& plan, const AttnArgs& a, const Laun
 hipError_t launch_attn_merge(const AttnPlan& plan, const AttnArgs& a, const Launch& l) {
   const int64_t rows = (int64_t)a.B * a.Hkv * a.rows;
   const int tile_rows = plan.waves * plan.rows_per_wave;
-  if (plan.head_dim != 128 && plan.head_dim != 64) return hipErrorInvalidValue;
-  if (plan.wide_merge) {
-    const dim3 grid((unsigned)rows);
-    return plan.head_dim == 128 ? launch_kernel(attn_merge_wide_kernel<128>, grid, dim3(256), l, a, tile_rows)
-                                : launch_kernel(attn_merge_wide_kernel<64>, grid, dim3(256), l, a, tile_rows);
+  // many chunks per row: eight chunk groups per row; U: chunks per group and round (2, 4 or 8)
+  const int cg = plan.wide_merge ? 8 : 1;
+  const int per = (plan.nsplit + cg - 1) / cg;
+  const int u = per <= 2 ? 2 : per <= 4 ? 4 : 8;
+  const int rw = 256 / ((plan.head_dim / 4) * cg);
+  const dim3 grid((unsigned)((rows + rw - 1) / rw));
+  switch (plan.head_dim * 1000 + cg * 10 + u) {
+#define BD_MERGE(d, c, uu) \
+  case d * 1000 + c * 10 + uu: return launch_kernel(attn_merge_kernel<d, c, uu>, grid, dim3(256), l, a, tile_rows);
+    BD_MERGE(128, 8, 2) BD_MERGE(128, 8, 4) BD_MERGE(128, 8, 8)
+    BD_MERGE(128, 1, 2) BD_MERGE(128, 1, 4) BD_MERGE(128, 1, 8)
+    BD_MERGE(64, 8, 2) BD_MERGE(64, 8, 4) BD_MERGE(64, 8, 8)
+    BD_MERGE(64, 1, 2) BD_MERGE(64, 1, 4) BD_MERGE(64, 1, 8)
+#undef BD_MERGE
+    default: return hipErrorInvalidValue;
   }
-  const dim3 grid((unsigned)((rows * (plan.head_dim / 4) + 255) / 256));
-  return plan.head_dim == 128 ? launch_kernel(attn_merge_narrow_kernel<128>, grid, dim3(256), l, a, tile_rows)
-                              : launch_kernel(attn_merge_narrow_kernel<64>, grid, dim3(256), l, a, tile_rows);
 }
 
 }  // namespace bd

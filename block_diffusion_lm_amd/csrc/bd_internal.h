@@ -46,7 +46,7 @@ struct AttnPlan {
   int nsplit;         // splits per (sequence, KV head)
   int64_t n_items;    // B * Hkv * nsplit * row_tiles workgroups
   bool direct;        // nsplit == 1: the split kernel writes the final output itself
-  bool wide_merge;    // many splits: merge with one workgroup per query row
+  bool wide_merge;    // many splits: the merge spreads each row's chunks over eight thread groups
   size_t part_acc_off, part_ml_off, bytes;   // workspace layout
 };
 
