@@ -106,9 +106,9 @@ __device__ void reduce_slice(const UnmaskArgs& a, int64_t row, int part) {
     const int per = 16 / elt;                       // elements per 16-byte vector
     const int64_t nvec = (v1 - v0) / per;           // full vectors of the slice
     const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + v0 * elt);
-    if (a.is_bf16) {
-      for (int64_t i = tid; i < nvec; i += 256) {
-        const u32x4 u = __builtin_nontemporal_load(vp + i);
+    // vectors t, t + 256, ... in order; four loads in flight at a time
+    auto fold_vec = [&](const u32x4 u, int64_t i) {
+      if (a.is_bf16) {
         float x[8];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -116,14 +116,20 @@ __device__ void reduce_slice(const UnmaskArgs& a, int64_t row, int part) {
           x[2 * w + 1] = __uint_as_float(u[w] & 0xffff0000u);
         }
         fold<8>(st, x, (int)(v0 + i * 8));
-      }
-    } else {
-      for (int64_t i = tid; i < nvec; i += 256) {
-        const u32x4 u = __builtin_nontemporal_load(vp + i);
+      } else {
         float x[4] = {__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]), __uint_as_float(u[3])};
         fold<4>(st, x, (int)(v0 + i * 4));
       }
+    };
+    int64_t i = tid;
+    for (; i + 3 * 256 < nvec; i += 4 * 256) {
+      u32x4 u[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) u[k] = __builtin_nontemporal_load(vp + i + k * 256);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) fold_vec(u[k], i + k * 256);
     }
+    for (; i < nvec; i += 256) fold_vec(__builtin_nontemporal_load(vp + i), i);
     // ragged tail of the slice (vocab not a multiple of the vector width)
     for (int64_t j = v0 + nvec * per + tid; j < v1; j += 256) {
       float x[1] = {load_logit(rowp, a.is_bf16, j)};
