@@ -148,3 +148,31 @@ def test_official_workloads_full_size_sampled(name):
     # the whole output is finite and the cache was not written
     assert np.all(np.isfinite(got))
     assert torch.equal(t["k_cache"].view(torch.int16).cpu(), torch.from_numpy(inp["k_cache"].view(np.int16)))
+
+
+EDGE = [
+    # name, Hq, Hkv, D, S, lengths (tile edges: 64-key tiles, chunks of whole tiles)
+    ("edges-8w-d128", 32, 2, 128, 16, (64, 127, 128, 129, 0, 191)),
+    ("edges-4w-d64", 8, 2, 64, 16, (64, 65, 256, 63, 1, 320)),
+    ("edges-8w-S64", 16, 4, 128, 64, (0, 64, 100, 192)),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 5])
+@pytest.mark.parametrize("causal", [False, True])
+def test_tile_edge_lengths(case, num_splits, causal):
+    """Prefix lengths on and next to tile edges, so that chunks hold zero, one or several tiles
+    wholly inside the prefix before the ones holding its end or the block's keys."""
+    name, Hq, Hkv, D, S, lens = case
+    lens = np.asarray(lens, np.int32)
+    w = I.small_workload(name, B=len(lens), Hq=Hq, Hkv=Hkv, D=D, S=S, prefix_len=int(lens.max()),
+                         wid=260 + EDGE.index(case))
+    inp = I.attn_inputs(w, lens=lens)
+    print(f"[attn] {name} splits={num_splits} causal={causal} lens={lens.tolist()}", flush=True)
+    got, lse, _ = run_gpu(inp, num_splits=num_splits, causal=causal)
+    f = {k: bf16_f64(inp[k]) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
+    ref, ref_lse = O.attn_step(f["q"], f["k_blk"], f["v_blk"], f["k_cache"], f["v_cache"], inp["prefix_len"],
+                               causal=causal)
+    assert_attn_close(got, ref, name)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
