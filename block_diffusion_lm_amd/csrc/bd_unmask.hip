@@ -86,6 +86,26 @@ __device__ __forceinline__ float load_logit(const void* row, int is_bf16, int64_
   return reinterpret_cast<const float*>(row)[j];
 }
 
+// The slice partials of row r combined in slice order; eight slices' loads are issued together.
+__device__ __forceinline__ Red row_partials(const UnmaskArgs& a, int64_t r) {
+  const float* pp = a.part + r * a.vsplit * 3;
+  Red st{-INFINITY, 0x7fffffff, 0.f};
+  for (int c0 = 0; c0 < a.vsplit; c0 += 8) {
+    float m[8], x[8], z[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = min(c0 + j, a.vsplit - 1);   // past the last slice: reloaded, then skipped
+      m[j] = pp[3 * c];
+      x[j] = pp[3 * c + 1];
+      z[j] = pp[3 * c + 2];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < a.vsplit) st = combine(st, Red{m[j], __float_as_int(x[j]), z[j]});
+  }
+  return st;
+}
+
 __device__ void reduce_slice(const UnmaskArgs& a, int64_t row, int part);
 __device__ void commit_sequence(const UnmaskArgs& a, int b);
 
@@ -168,9 +188,7 @@ __device__ void commit_sequence(const UnmaskArgs& a, int b) {
   float p = 0.f;
   int tok = -1;
   if (masked) {
-    const float* pp = a.part + r * a.vsplit * 3;
-    Red st{pp[0], __float_as_int(pp[1]), pp[2]};
-    for (int c = 1; c < a.vsplit; ++c) st = combine(st, Red{pp[3 * c], __float_as_int(pp[3 * c + 1]), pp[3 * c + 2]});
+    const Red st = row_partials(a, r);
     p = 1.0f / st.z;
     tok = st.idx;
   }
@@ -221,10 +239,7 @@ __global__ __launch_bounds__(64) void spec_accept_kernel(UnmaskArgs a) {
   // argmax of row r (the choice for position s + 1)
   int choice_next = -1;
   if (in) {
-    const float* pp = a.part + r * a.vsplit * 3;
-    Red st{pp[0], __float_as_int(pp[1]), pp[2]};
-    for (int c = 1; c < a.vsplit; ++c) st = combine(st, Red{pp[3 * c], __float_as_int(pp[3 * c + 1]), pp[3 * c + 2]});
-    choice_next = st.idx;
+    choice_next = row_partials(a, r).idx;
   }
   // AR's choice for position s: lane s - 1's row argmax, lane 0 takes first_choice[b]
   const int up = __shfl_up(choice_next, 1, 64);
