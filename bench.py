@@ -389,7 +389,9 @@ def main():
         "roofline": {"kernel": "attn_split", "bound": "hbm", "achieved": round(achieved_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(os.path.join(ROOT, "block_diffusion_lm_amd", "csrc", "bd_attn.hip")),
-                     "algorithmic_bytes_per_launch": round(bytes_per_launch)},
+                     "algorithmic_bytes_per_launch": round(bytes_per_launch),
+                     # the same launches against the dense bf16 MFMA peak (the kernel sits near the ridge)
+                     "mfma_frac": round(fl_step / T / (split_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }
     line["rows"] = row_figures(args, w, bd, torch, dev, recs, steps_used, commits, mask0, lens, ad, ws, dq, dlog,
                                caches, lens_d, is_bf16, T)
