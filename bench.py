@@ -229,7 +229,7 @@ def main():
                     help="only run a plain 512 MiB device copy (5 times): the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build runs on a single MI355X (no multi-GPU path); "
+        print("bench.py measures one GPU: the library has no multi-GPU path (one MI355X per process); "
               "use --gpus 1", file=sys.stderr)
         sys.exit(2)
 

@@ -62,7 +62,7 @@ extern "C" {
 typedef enum {
   BD_OK = 0,
   BD_EINVAL = 1,        /* invalid argument (null pointer, shape, range, alignment) */
-  BD_EUNSUPPORTED = 2,  /* valid but not supported by this build (e.g. head_dim 96) */
+  BD_EUNSUPPORTED = 2,  /* valid but not supported by the library (e.g. head_dim 96) */
   BD_EWORKSPACE = 3,    /* workspace smaller than the *_workspace_bytes query */
   BD_EHIP = 4           /* a HIP runtime call or kernel launch failed */
 } bd_status;

@@ -41,7 +41,7 @@ states. Sources (page title, section):
   between consecutive loop iterations falls below epsilon, or when the
   iteration budget is reached.
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent:
 one softmax over prefix keys followed by block keys; every prefix key visible
 to every block query; no mask inside the block; scale tau = float32(1/sqrt(D))
 unless given; GQA head h reads KV head floor(h * Hkv / Hq); confidence = the
