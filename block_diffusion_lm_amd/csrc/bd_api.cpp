@@ -42,7 +42,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 constexpr int kCUs = 256;                  // MI355X compute units
 constexpr size_t kLdsPerCU = 160 * 1024;   // bytes of LDS per compute unit
-constexpr int64_t kMinChunk = 512;         // keys per split below which splitting does not pay
+constexpr int64_t kMinChunk = 256;         // keys per split below which splitting does not pay
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -93,9 +93,15 @@ void plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
   p->head_dim = d->head_dim;
   p->rows = d->block_len * group;
   // 32 query rows per wave, two waves per SIMD; eight waves (one workgroup per CU) share each LDS
-  // key tile when the group has more than 128 rows, else four (two workgroups per CU).
+  // key tile when the group has more than 128 rows and such workgroups, over chunks of at least
+  // kMinChunk keys, can fill the chip; otherwise four (two workgroups per CU, twice as many row
+  // tiles: short prefixes of few sequences, e.g. single-sequence decode).
   p->rows_per_wave = 32;
-  p->waves = p->rows > 128 ? 8 : 4;
+  {
+    const int64_t nk = d->max_prefix_len + d->block_len;
+    const int64_t wide_items = (int64_t)d->batch * d->n_kv_heads * ((p->rows + 255) / 256) * (nk / kMinChunk);
+    p->waves = p->rows > 128 && wide_items >= kCUs ? 8 : 4;
+  }
   p->key_tile = bd::kAttnKeyTile;
   const int tile_rows = p->waves * p->rows_per_wave;
   p->row_tiles = (p->rows + tile_rows - 1) / tile_rows;
@@ -112,7 +118,7 @@ void plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
     const int by_lds = (int)(kLdsPerCU / lds);
     const int64_t slots = (int64_t)kCUs * (by_regs < by_lds ? by_regs : by_lds);
     nsplit = (slots + base - 1) / base;
-    const int64_t cap = (nkeys + kMinChunk - 1) / kMinChunk;
+    const int64_t cap = nkeys / kMinChunk;   // chunks of at least kMinChunk keys
     if (nsplit > cap) nsplit = cap;
     if (nsplit < 1) nsplit = 1;
   }
