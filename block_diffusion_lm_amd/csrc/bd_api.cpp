@@ -78,6 +78,10 @@ bd_status check_attn_desc(const bd_attn_desc* d) {
     return fail(BD_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", d->head_dim);
   if (d->block_len < 1 || d->block_len > 64) return fail(BD_EINVAL, "block_len must be in [1, 64] (got %d)", d->block_len);
   if (d->prefix_capacity < 1) return fail(BD_EINVAL, "prefix_capacity must be >= 1");
+  // the kernels address one (sequence, KV head) slab of the cache with 32-bit buffer offsets
+  if (d->prefix_capacity > (int64_t)0x7fffffff / (2 * d->head_dim))
+    return fail(BD_EUNSUPPORTED, "prefix_capacity %lld too large: a (sequence, KV head) slab of the cache must stay "
+                "below 2 GiB", (long long)d->prefix_capacity);
   if (d->max_prefix_len < 0 || d->max_prefix_len > d->prefix_capacity)
     return fail(BD_EINVAL, "max_prefix_len must be in [0, prefix_capacity]");
   if (!std::isfinite(d->softmax_scale)) return fail(BD_EINVAL, "softmax_scale must be finite");

@@ -93,7 +93,8 @@ typedef struct {
   int32_t n_kv_heads;       /* Hkv >= 1 */
   int32_t head_dim;         /* D: 64 or 128 */
   int32_t block_len;        /* S: 1 .. 64 */
-  int64_t prefix_capacity;  /* Lcap >= 1: token stride of k_cache / v_cache */
+  int64_t prefix_capacity;  /* Lcap >= 1: token stride of k_cache / v_cache; Lcap * D * 2 bytes < 2 GiB
+                               (one (sequence, KV head) slab), else BD_EUNSUPPORTED */
   int64_t max_prefix_len;   /* host upper bound on every prefix_len[b]; 0 .. Lcap; used to plan the split */
   float softmax_scale;      /* tau; <= 0 selects 1/sqrt(D) computed in float32 */
   int32_t num_splits;       /* 0 = automatic; > 0 forces the number of key chunks per (b, KV head) */

@@ -65,6 +65,7 @@ def call_attn(L, d, ptr=16 * 1024, ws=None, nbytes=None):
     ("num_splits", -1, _lib.BD_EINVAL),
     ("softmax_scale", math.nan, _lib.BD_EINVAL),
     ("causal", 2, _lib.BD_EINVAL),
+    ("prefix_capacity", 1 << 23, _lib.BD_EUNSUPPORTED),   # 2 GiB slab at D = 128
 ])
 def test_attn_descriptor_validation(L, field, value, status):
     d = good_attn()
