@@ -61,34 +61,36 @@ def cpu_baseline(w, inputs, logits0, mask0, budget_s=20.0):
     except Exception:
         cores = len(os.sched_getaffinity(0))
     lens = inputs["prefix_len"]
+    # whole passes over step 0's attention (every (sequence, KV head) group), repeated until about
+    # 70 % of the budget is spent (at least one pass), then the vocabulary reduction of the masked
+    # rows, repeated for the rest
     t0 = time.perf_counter()
     fl = 0
     pairs = 0
-    for b in range(w.B):
-        for g in range(w.Hkv):
-            rows = [(b, s, h) for s in range(w.S) for h in range(g * w.group, (g + 1) * w.group)]
-            O.attn_rows(inputs["q"], inputs["k_blk"], inputs["v_blk"], inputs["k_cache"], inputs["v_cache"], lens, rows)
-            fl += 4 * len(rows) * (int(lens[b]) + w.S) * w.D
-            pairs += 1
-            if time.perf_counter() - t0 > budget_s * 0.7:
-                break
-        if time.perf_counter() - t0 > budget_s * 0.7:
-            break
+    passes = 0
+    while passes == 0 or time.perf_counter() - t0 < budget_s * 0.7:
+        for b in range(w.B):
+            for g in range(w.Hkv):
+                rows = [(b, s, h) for s in range(w.S) for h in range(g * w.group, (g + 1) * w.group)]
+                O.attn_rows(inputs["q"], inputs["k_blk"], inputs["v_blk"], inputs["k_cache"], inputs["v_cache"], lens,
+                            rows)
+                fl += 4 * len(rows) * (int(lens[b]) + w.S) * w.D
+                pairs += 1
+        passes += 1
     t_attn = time.perf_counter() - t0
     t1 = time.perf_counter()
     masked = np.flatnonzero(mask0)
     dec = O.bf16_to_f64 if w.logits_dtype == "bf16" else None
     n = 0
-    for r in masked:
-        O.confidences(logits0[r:r + 1], np.ones(1, np.uint8), dec)
-        n += 1
-        if time.perf_counter() - t1 > budget_s * 0.3:
-            break
+    while n == 0 or time.perf_counter() - t1 < budget_s * 0.3:
+        for r in masked:
+            O.confidences(logits0[r:r + 1], np.ones(1, np.uint8), dec)
+            n += 1
     t_um = time.perf_counter() - t1
     return {"value": fl / t_attn / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 oracle: attention of {pairs} (sequence, KV head) groups "
-                      f"({pairs * w.S * w.group} query rows over {int(lens[0]) + w.S} keys) in {t_attn:.1f} s; "
-                      f"vocabulary reduction of {n} masked rows in {t_um:.2f} s",
+            "sample": f"float64 oracle: {passes} pass(es) over step 0's attention ({w.B * w.Hkv} (sequence, KV head) "
+                      f"groups, {w.B * w.S * w.Hq} query rows over {int(lens[0]) + w.S} keys each) in {t_attn:.1f} s; "
+                      f"vocabulary reduction of {n} masked rows ({len(masked)} distinct) in {t_um:.1f} s",
             "unmask_positions_per_s": n / t_um if t_um > 0 else None}
 
 
