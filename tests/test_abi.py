@@ -232,3 +232,33 @@ def test_halt_pointer_validation(L):
     d.dtype = _lib.BD_F32
     d.n_per_seq = 4
     assert L.bd_loop_halt_workspace_bytes(ctypes.byref(d)) > 0
+
+
+def test_header_is_c99_and_links_from_c(tmp_path):
+    """include/bd.h compiles as strict C99 and a C program links against libbd.so and calls it
+    (host-only entry points: version string and workspace planning)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include "bd.h"
+#include <stdio.h>
+int main(void) {
+  bd_attn_desc d = {2, 32, 2, 128, 16, 4096, 4096, 0.0f, 0, 0};
+  size_t ws = bd_attn_workspace_bytes(&d);
+  d.head_dim = 96;
+  size_t bad = bd_attn_workspace_bytes(&d);
+  printf("%s %zu %zu\n", bd_version(), ws, bad);
+  return (ws > 0 && bad == 0) ? 0 : 1;
+}
+''')
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(root, "include"),
+                    str(src), "-o", str(exe), "-L", libdir, "-lbd", f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    assert out[0] == "bd" and int(out[-2]) > 0 and int(out[-1]) == 0
