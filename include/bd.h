@@ -267,7 +267,10 @@ size_t bd_denoise_workspace_bytes(const bd_attn_desc* attn, const bd_unmask_desc
  * out:        bf16 [B,S,Hq,D], rewritten every step for the active sequences.
  * mask/tokens: as in bd_confidence_unmask, updated step by step.
  * steps_used: int32 [B] (required): t+1 of the last step at which b was active, 0 if never.
- * commits_per_step: int32 [T, B] or NULL: rows t0 .. T-1 receive n_commit of each step. */
+ * commits_per_step: int32 [T, B] or NULL: rows t0 .. T-1 receive n_commit of each step.
+ * The call only enqueues kernels on `stream` (no allocation, memset or host synchronisation while
+ * no trace is attached), so with hooks that do not synchronise either (bd_table_hooks) the whole
+ * loop can be captured into a HIP graph and replayed. */
 bd_status bd_denoise_block(const bd_attn_desc* attn, const bd_unmask_desc* unmask,
                            int32_t T, int32_t t0, const bd_step_hooks* hooks,
                            const void* k_cache, const void* v_cache, const int32_t* prefix_len,

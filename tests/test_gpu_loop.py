@@ -138,3 +138,51 @@ def test_native_step_table_matches_python_hooks():
                         res["out"].view(torch.int16).cpu()))
     for a, b in zip(*results):
         assert torch.equal(a, b)
+
+
+def test_denoise_block_captured_in_a_graph_replays_like_eager():
+    """The whole T-step loop (table hooks: no host callback into Python, no allocation, no memset,
+    no host synchronisation) can be captured into a HIP graph; every replay -- with eager work and
+    synchronisations between the replays -- gives the eager call's bytes."""
+    w = I.small_workload("loopg", B=2, Hq=32, Hkv=2, D=128, S=16, prefix_len=(300, 1200), V=2048, logits_dtype="bf16",
+                         sigma=3.0, gamma=0.9, mask_rule="all", peaks=True, T=4, wid=253)
+    lens = I.prefix_lengths(w)
+    cache = I.prefix_cache(w, lens)
+    steps = [I.attn_inputs(w, step=t, lens=lens, cache=False) for t in range(w.T)]
+    qkv = [tuple(dev_bf16(steps[t][k]) for k in ("q", "k_blk", "v_blk")) for t in range(w.T)]
+    lg = [dev_bf16(I.logits(w, step=t)) for t in range(w.T)]
+    table = ([x[0] for x in qkv], [x[1] for x in qkv], [x[2] for x in qkv], lg)
+    kc, vc, ln = dev_bf16(cache["k_cache"]), dev_bf16(cache["v_cache"]), dev(lens)
+    mask_src = dev(I.initial_mask(w))
+    m_d = torch.empty_like(mask_src)
+    t_d = torch.zeros(w.B * w.S, dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.S, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    su = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    cps = torch.zeros((w.T, w.B), dtype=torch.int32, device="cuda")
+    ad = bd.attn_desc(w.B, w.Hq, w.Hkv, w.D, w.S, kc.shape[2])
+    ud = bd.unmask_desc(w.B, w.S, w.V, None, True, w.gamma)
+    ws = torch.empty(bd.denoise_workspace_bytes(ad, ud), dtype=torch.uint8, device="cuda")
+
+    def call():
+        m_d.copy_(mask_src)
+        bd.denoise_block(None, None, kc, vc, ln, m_d, t_d, w.T, w.Hq, w.gamma, w.S, w.V, out=out, workspace=ws,
+                         step_table=table, steps_used=su, commits_per_step=cps)
+
+    call()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (m_d, t_d, out.view(torch.int16), su, cps)]
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in (t_d, out, su, cps):
+            x.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (m_d, t_d, out.view(torch.int16), su, cps)
+        assert all(torch.equal(a, b) for a, b in zip(got, ref)), f"replay {rep}"
+        call()   # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(t_d, ref[1])
