@@ -176,3 +176,41 @@ def test_tile_edge_lengths(case, num_splits, causal):
                                causal=causal)
     assert_attn_close(got, ref, name)
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
+
+
+def _random_cases(n=40, seed=2026):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        S = int(rng.choice([1, 2, 5, 16, 32, 64]))
+        B = int(rng.integers(1, 5))
+        lmax = int(rng.choice([0, 63, 64, 200, 777, 2100]))
+        lens = rng.integers(0, lmax + 1, size=B).astype(np.int32)
+        splits = int(rng.choice([0, 0, 1, 3, 9]))
+        causal = bool(rng.integers(0, 2))
+        cases.append((f"r{i}-B{B}-g{g}x{Hkv}-D{D}-S{S}-L{lmax}-s{splits}-{'c' if causal else 'b'}",
+                      B, g * Hkv, Hkv, D, S, lens, splits, causal))
+    return cases
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_shapes_match_oracle(case):
+    """A seeded sweep over head dims, GQA groups, block lengths, ragged prefix lengths (on and off
+    tile edges, zero included), forced split counts and both attention modes."""
+    name, B, Hq, Hkv, D, S, lens, splits, causal = case
+    w = I.small_workload(name, B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, prefix_len=max(int(lens.max()), 1),
+                         wid=400 + RANDOM.index(case))
+    inp = I.attn_inputs(w, lens=lens)
+    print(f"[attn] {name} lens={lens.tolist()}", flush=True)
+    got, lse, _ = run_gpu(inp, num_splits=splits, causal=causal)
+    f = {k: bf16_f64(inp[k]) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
+    ref, ref_lse = O.attn_step(f["q"], f["k_blk"], f["v_blk"], f["k_cache"], f["v_cache"], inp["prefix_len"],
+                               causal=causal)
+    assert_attn_close(got, ref, name)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
