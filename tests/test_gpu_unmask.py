@@ -124,3 +124,50 @@ def test_determinism_identical_rows():
     torch.cuda.synchronize()
     assert torch.equal(confs[0], confs[1])
     assert confs[0][5].item() == confs[0][2].item()
+
+
+def _unmask_cases(n=30, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        S = int(rng.choice([1, 3, 16, 32, 64]))
+        B = int(rng.integers(1, 5))
+        V = int(rng.choice([1, 2, 7, 8, 9, 100, 8191, 8193, 40000, 131072]))
+        bf16 = bool(rng.integers(0, 2))
+        pad = int(rng.choice([0, 0, 8, 24]))
+        gamma = float(rng.choice([0.0, 0.3, 0.9, 0.999]))
+        commit_all = bool(rng.random() < 0.2)
+        min_commit = bool(rng.random() < 0.8)
+        out.append((f"u{i}-B{B}-S{S}-V{V}-{'bf16' if bf16 else 'f32'}-p{pad}-g{gamma}"
+                    f"{'-all' if commit_all else ''}{'' if min_commit else '-nomin'}",
+                    B, S, V, bf16, pad, gamma, commit_all, min_commit))
+    return out
+
+
+UCASES = _unmask_cases()
+
+
+@pytest.mark.parametrize("case", UCASES, ids=[c[0] for c in UCASES])
+def test_random_unmask_shapes(case):
+    """A seeded sweep over vocabulary sizes (tiny, ragged, one slice, many slices), padded row
+    strides, logits dtypes, block lengths, thresholds and the commit flags; random masks."""
+    name, B, S, V, bf16, pad, gamma, commit_all, min_commit = case
+    stride = V + pad if not bf16 else (V + pad + 7) // 8 * 8
+    if not bf16:
+        stride = (stride + 3) // 4 * 4
+    # inputs are redrawn (deterministically) until no decision lies within the oracle's near-tie
+    # band around gamma or the fallback's runner-up, where both answers would be right
+    for attempt in range(50):
+        rng = np.random.default_rng([900 + UCASES.index(case), attempt])
+        x = (rng.standard_normal((B * S, stride)) * 3).astype(np.float32)
+        # a confident token on a third of the rows, placed at random
+        rows = rng.random(B * S) < 0.33
+        x[rows, rng.integers(0, V, size=int(rows.sum()))] += 12.0
+        x[:, V:] = 1e30   # never read
+        mask = (rng.random(B * S) < 0.7).astype(np.uint8)
+        logits = I.f32_to_bf16_bits(x) if bf16 else x
+        ref = O.confidence_unmask(logits[:, :V], mask, np.zeros(B * S, np.int32), S, gamma, min_commit, commit_all,
+                                  decode=O.bf16_to_f64 if bf16 else None)
+        if not O.near_ties(ref["conf"], mask, S, gamma, min_commit, commit_all):
+            break
+    run_both(logits, bf16, mask, S, gamma, min_commit=min_commit, commit_all=commit_all, vocab=V)
