@@ -52,6 +52,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyRescale = 8.0f;
+// Full-tile loop: a lane's sum of one block's 16 P values above this (or not finite) sends the
+// block through the slow path, which raises the running max to the block's and recomputes P.
+constexpr float kBlockSumLimit = 256.0f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -300,6 +303,7 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
   // buffer resources over this (sequence, KV head)'s cached rows (buffer offsets are 32-bit)
   const __amdgpu_buffer_rsrc_t rsrc_k = raw_rsrc(kc, (uint64_t)a.lcap * D * 2);
   const __amdgpu_buffer_rsrc_t rsrc_v = raw_rsrc(vc, (uint64_t)a.lcap * D * 2);
+  const uint32_t blk_pitch = (uint32_t)(blk_stride * 2);   // bytes between block positions
   // Per-lane source offsets. K instruction j fills K rows r = 4j + lane / 16 (D = 128; 8j + lane / 8
   // for D = 64) with their 16-byte chunks at swizzled positions: chunk c of row r sits at position
   // c ^ (r & 7), so the K fragment reads below hit eight different bank groups. A lane's position
@@ -336,20 +340,25 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
         dma16_buf(rsrc_v, vl, soff + 1024 * j, dst + G::KBYTES + 1024 * j);
       }
     } else {
-      auto src_of = [&](uint32_t off, const uint16_t* cache, const uint16_t* blk) {
-        const int64_t key = min(kt0 + (int64_t)(off / (D * 2)), k_end - 1);
-        const uint16_t* row = key < len ? cache + key * D : blk + (key - len) * blk_stride;
-        return reinterpret_cast<const char*>(row) + off % (D * 2);
+      // per lane: cached rows through the cache resources, rows past the prefix end by a global
+      // address (the two are exec-masked: each lane issues one), rows past the chunk end repeating
+      // its last key. Keys and cache byte offsets fit 32 bits (prefix capacity check).
+      const int kt = (int)kt0, kend = (int)k_end, ln = (int)len;
+      auto copy = [&](__amdgpu_buffer_rsrc_t rc, const uint16_t* blk, uint32_t off, char* d) {
+        const int key = min(kt + (int)(off / (D * 2)), kend - 1);
+        const uint32_t col = off % (D * 2);
+        if (key < ln) dma16_buf(rc, (uint32_t)key * (D * 2) + col, 0, d);
+        else dma16(reinterpret_cast<const char*>(blk) + (size_t)(key - ln) * blk_pitch + col, d);
       };
 #pragma unroll
       for (int i = 0; i < NK; ++i) {
         const int j = wave + NWD * i;
-        dma16(src_of(kl + 1024 * j, kc, kb0), dst + 1024 * j);
+        copy(rsrc_k, kb0, kl + 1024 * j, dst + 1024 * j);
       }
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int j = wave + NWD * i;
-        dma16(src_of(vl + 1024 * j, vc, vb0), dst + G::KBYTES + 1024 * j);
+        copy(rsrc_v, vb0, vl + 1024 * j, dst + G::KBYTES + 1024 * j);
       }
     }
   };
@@ -490,6 +499,26 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
       l_run[rb] = ls;
     }
   };
+  // Full-tile variant of exp_p: the running max is finite (set by the first block), and the
+  // block's row sums are returned instead of added, so the caller can check them first.
+  auto exp_full = [&](const f32x16 (&sacc)[RB], bf16x8 (&pf)[2][RB], float (&bs)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float mneg = -m_run[rb];
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pf[e][rb][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[rb][8 * e + i], sc, mneg));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2 p2 = {pf[e][rb][2 * i], pf[e][rb][2 * i + 1]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, ls, false);
+        }
+      }
+      bs[rb] = ls;
+    }
+  };
   // O^T += V^T P^T
   auto pv = [&](const bf16x8 (&vf)[2][G::DB], const bf16x8 (&pf)[2][RB]) {
 #pragma unroll
@@ -535,6 +564,35 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
         rescale(mx, true);
         load_k(0, 1, kf);
       }
+      // P of block j with the running max. The row maxima are not computed on this path: a block
+      // whose P sum on some lane exceeds kBlockSumLimit (a key above the running max by more than
+      // log2(kBlockSumLimit / 16) in log2 units; an overflow shows as inf) takes the rare branch,
+      // which raises the running max to the block's (rescaling O and l) and recomputes P, so every
+      // P stays <= kBlockSumLimit.
+      auto p_of = [&](bf16x8 (&pf)[2][RB]) {
+        float bs[RB];
+        exp_full(s_cur, pf, bs);
+        bool big = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) big |= !(bs[rb] <= kBlockSumLimit);
+        if (__builtin_amdgcn_ballot_w64(big)) {
+          row_max(s_cur, mx);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const float mnew = fmaxf(m_run[rb], mx[rb]);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - mnew);
+            l_run[rb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[rb][db][r] *= alpha;
+            m_run[rb] = mnew;
+          }
+          exp_full(s_cur, pf, bs);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) l_run[rb] += bs[rb];
+      };
       // block j = 2t + kb of tile t; `last`: the odd block of the last full tile (no block j + 2)
       auto block = [&](int t, int kb, bool last) {
         const int st = t % NSTAGE;
@@ -546,7 +604,7 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
           v_addr(st, kb, va);
           read_vt<D, 0>(va, vf);
           qk(kf, s_nxt);
-          exp_p(s_cur, pf);
+          p_of(pf);
         }
         if (kb == 0) {
           wait_tile(min(NSTAGE - 3, ntiles - 2 - t));
@@ -554,11 +612,7 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
         }
         if (wave_rows) {
           pv(vf, pf);
-          if (!last) {
-            load_k((t + 1) % NSTAGE, kb, kf);
-            row_max(s_nxt, mx);
-            rescale(mx, true);
-          }
+          if (!last) load_k((t + 1) % NSTAGE, kb, kf);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) s_cur[rb] = s_nxt[rb];
         }
