@@ -178,6 +178,53 @@ def test_tile_edge_lengths(case, num_splits, causal):
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
 
 
+RISE = ["ramp", "jumps", "wide"]
+RISE_SHAPES = [
+    # name, B, Hq, Hkv, D, S, prefix_len: the first plans eight-wave workgroups (the full-tile loop of
+    # the long-prefix kernel), the second four-wave ones with head_dim 64 (the same loop)
+    ("8w-d128", 2, 128, 8, 128, 16, (4000, 4200)),
+    ("4w-d64", 2, 32, 2, 64, 16, (1100, 1300)),
+]
+
+
+@pytest.mark.parametrize("shape", RISE_SHAPES, ids=[s[0] for s in RISE_SHAPES])
+@pytest.mark.parametrize("pattern", RISE)
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_running_max_rises_inside_the_prefix(shape, pattern, num_splits):
+    """Scores that keep rising across the cached prefix, so that blocks of wholly cached keys raise
+    the running max again and again: a ramp (every 32-key block ~4 log2 units above the one before,
+    so its P sum per lane passes 256, mostly with no key above the max by 8), single keys at ~12,
+    ~98 and ~255 log2 units (the last ~157 above the max: its P overflows float32 until the max is
+    raised), and a wide case where half of a block's keys sit ~5 units above the max (figures for
+    head_dim 128; 1.4 times as many units at 64)."""
+    sname, B, Hq, Hkv, D, S, L = shape
+    w = I.small_workload(f"rise-{pattern}-{sname}", B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, prefix_len=L,
+                         wid=290 + 3 * RISE_SHAPES.index(shape) + RISE.index(pattern))
+    inp = I.attn_inputs(w)
+    q = bf16_f64(inp["q"])
+    kc = bf16_f64(inp["k_cache"])
+    q[..., 0] = 8.0
+    nk = kc.shape[2]
+    blk = np.arange(nk) // 32
+    if pattern == "ramp":
+        kc[:, :, :, 0] = 4.0 * blk                            # +32 raw = +4.08 log2 units a block
+    elif pattern == "jumps":
+        kc[:, :, :, 0] = 0.0
+        for b0, v in ((5, 12.0), (14, 96.0), (26, 250.0)):   # ~12, ~98 and ~255 log2 units
+            kc[:, :, 32 * b0 + 7, 0] = v
+    else:
+        kc[:, :, :, 0] = 0.0
+        kc[:, :, 32 * 9:32 * 9 + 32:2, 0] = 5.0             # 16 keys of one block at ~+5 units
+    inp["q"] = I.f32_to_bf16_bits(q.astype(np.float32))
+    inp["k_cache"] = I.f32_to_bf16_bits(kc.astype(np.float32))
+    print(f"[attn] rise-{pattern}-{sname} splits={num_splits} lens={inp['prefix_len'].tolist()}", flush=True)
+    got, lse, _ = run_gpu(inp, num_splits=num_splits)
+    ref, ref_lse = oracle_full(inp)
+    assert np.isfinite(got).all()
+    assert_attn_close(got, ref, f"rise-{pattern}-{sname}")
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL * max(1.0, np.abs(ref_lse).max() / 64))
+
+
 def _random_cases(n=40, seed=2026):
     rng = np.random.default_rng(seed)
     cases = []
