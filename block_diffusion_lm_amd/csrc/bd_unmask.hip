@@ -142,12 +142,23 @@ __device__ void reduce_slice(const UnmaskArgs& a, int64_t row, int part) {
       }
     };
     int64_t i = tid;
-    for (; i + 3 * 256 < nvec; i += 4 * 256) {
+    // software-pipelined: the next group's four loads are issued before this group is folded
+    if (i + 3 * 256 < nvec) {
       u32x4 u[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) u[k] = __builtin_nontemporal_load(vp + i + k * 256);
+      for (; i + 7 * 256 < nvec; i += 4 * 256) {
+        u32x4 nx[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) nx[k] = __builtin_nontemporal_load(vp + i + (4 + k) * 256);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) fold_vec(u[k], i + k * 256);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) u[k] = nx[k];
+      }
 #pragma unroll
       for (int k = 0; k < 4; ++k) fold_vec(u[k], i + k * 256);
+      i += 4 * 256;
     }
     for (; i < nvec; i += 256) fold_vec(__builtin_nontemporal_load(vp + i), i);
     // ragged tail of the slice (vocab not a multiple of the vector width)
