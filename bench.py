@@ -165,7 +165,10 @@ def row_figures(args, w, bd, torch, dev, recs, steps_used, commits, mask0, lens,
     for name, ms in tr.records():
         ap.setdefault(name, []).append(ms)
     tr.clear()
-    app = [a + b for a, b in zip(ap.get("kv_append", [])[1:], ap.get("len_advance", [])[1:])]
+    # one launch per call for small blocks (copy and length advance together), else two
+    app = ap.get("kv_append", [])[1:]
+    if ap.get("len_advance"):
+        app = [a + b for a, b in zip(app, ap["len_advance"][1:])]
     rows["kv_append"] = fig(app, 2 * 2 * w.B * w.S * w.Hkv * w.D * 2)
     draft = torch.zeros(w.B * w.S, dtype=torch.int32, device=dev)
     first = torch.zeros(w.B, dtype=torch.int32, device=dev)

@@ -390,6 +390,8 @@ bd_status bd_kv_append(const bd_attn_desc* desc, const void* k_new, const void* 
   a.D = desc->head_dim;
   a.lcap = desc->prefix_capacity;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bd::kv_append_one_launch(a))
+    return traced("kv_append", s, [&](const bd::Launch& l) { return bd::launch_kv_append_seq(a, l); });
   st = traced("kv_append", s, [&](const bd::Launch& l) { return bd::launch_kv_append(a, l); });
   if (st != BD_OK) return st;
   return traced("len_advance", s, [&](const bd::Launch& l) { return bd::launch_len_advance(a, l); });

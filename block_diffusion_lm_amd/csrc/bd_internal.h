@@ -130,6 +130,11 @@ struct AppendArgs {
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, const Launch& l);
+// blocks of at most kSeqUnits 16-byte units of K per sequence: copy and length advance in one
+// launch (one workgroup per sequence)
+constexpr int kSeqUnits = 2048;
+bool kv_append_one_launch(const AppendArgs& a);
+hipError_t launch_kv_append_seq(const AppendArgs& a, const Launch& l);
 
 // ---------------------------------------------------------------------------------------------
 // adaptive loop halting

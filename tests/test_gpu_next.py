@@ -87,11 +87,25 @@ def capacity_cache(w, lens, extra):
     return out
 
 
+APPEND_SHAPES = [
+    # B, Hq, Hkv, D, S: one launch per call up to 2048 16-byte units of K per sequence (one to
+    # eight per thread of the sequence's workgroup), two launches above
+    (3, 8, 2, 128, 16),
+    (3, 4, 1, 64, 5),
+    (3, 16, 8, 128, 16),
+    (3, 16, 8, 128, 32),
+]
+
+
+@pytest.mark.parametrize("shape", APPEND_SHAPES, ids=[f"B{s[0]}-Hkv{s[2]}-D{s[3]}-S{s[4]}" for s in APPEND_SHAPES])
 @pytest.mark.parametrize("active", [None, [1, 0, 1]])
-def test_kv_append_bit_exact(active):
-    w = I.small_workload("append", B=3, Hq=8, Hkv=2, D=128, S=16, prefix_len=(0, 300), wid=320)
+def test_kv_append_bit_exact(active, shape):
+    B, Hq, Hkv, D, S = shape
+    w = I.small_workload("append", B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, prefix_len=(0, 300),
+                         wid=320 + APPEND_SHAPES.index(shape))
     lens = I.prefix_lengths(w)
     cache = capacity_cache(w, lens, 40)
+    print(f"[append] shape={shape} active={active} lens={lens.tolist()}", flush=True)
     new = I.attn_inputs(w, lens=lens, cache=False)
     kc, vc, ln = dev_bf16(cache["k_cache"]), dev_bf16(cache["v_cache"]), dev(lens.copy())
     act = None if active is None else dev(np.array(active, np.uint8))
