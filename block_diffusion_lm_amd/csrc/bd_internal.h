@@ -1,5 +1,6 @@
 // Internal interface between the host side of the library (bd_api.cpp) and the HIP kernels
-// (bd_attn.hip, bd_unmask.hip). Not installed; the public ABI is include/bd.h.
+// (bd_attn.hip, bd_unmask.hip, bd_cache.hip, bd_halt.hip). Not installed; the public ABI is
+// include/bd.h.
 #pragma once
 
 #include <hip/hip_ext.h>
