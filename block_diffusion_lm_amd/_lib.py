@@ -77,6 +77,20 @@ EXPORTS = [
 _lib = None
 
 
+def hip_runtimes() -> list:
+    """Distinct HIP runtime libraries (libamdhip64) mapped into this process, by real path."""
+    found = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) >= 6 and "libamdhip64" in os.path.basename(parts[5]):
+                    found.add(os.path.realpath(parts[5]))
+    except OSError:
+        return []
+    return sorted(found)
+
+
 def load() -> ctypes.CDLL:
     """Load libbd.so (built in-tree). Raises if it has not been built: there is no fallback."""
     global _lib
@@ -88,6 +102,11 @@ def load() -> ctypes.CDLL:
     # streams and device pointers handed over from torch are valid inside the library.
     import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
+    # two runtimes would give the library streams and pointers that are not its own
+    rts = hip_runtimes()
+    if len(rts) > 1:
+        raise RuntimeError(f"more than one HIP runtime is mapped into this process: {rts}; libbd must share "
+                           "torch's (import torch first, link libbd without a private runtime copy)")
     vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
     P = ctypes.POINTER
     L.bd_attn_workspace_bytes.argtypes = [P(AttnDesc)]

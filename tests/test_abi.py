@@ -39,6 +39,12 @@ def test_every_declared_symbol_is_exported(L):
     assert set(names) == set(_lib.EXPORTS)
 
 
+def test_one_hip_runtime_is_mapped(L):
+    # libbd binds to the runtime torch loaded (same soname), so exactly one libamdhip64 is mapped
+    rts = _lib.hip_runtimes()
+    assert len(rts) == 1, rts
+
+
 def test_version(L):
     assert b"gfx950" in L.bd_version()
 
