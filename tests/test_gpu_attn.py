@@ -178,6 +178,19 @@ def test_tile_edge_lengths(case, num_splits, causal):
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
 
 
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_largest_query_group(num_splits):
+    """The largest row count per KV head the descriptor allows in one group: S = 64 block positions
+    times 64 query heads on one KV head (4096 rows, many row tiles)."""
+    w = I.small_workload("rows4096", B=1, Hq=64, Hkv=1, D=128, S=64, prefix_len=900, wid=289)
+    inp = I.attn_inputs(w)
+    print(f"[attn] rows4096 splits={num_splits}", flush=True)
+    got, lse, _ = run_gpu(inp, num_splits=num_splits)
+    ref, ref_lse = oracle_full(inp)
+    assert_attn_close(got, ref, "rows4096")
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
+
+
 RISE = ["ramp", "jumps", "wide"]
 RISE_SHAPES = [
     # name, B, Hq, Hkv, D, S, prefix_len: the first plans eight-wave workgroups (the full-tile loop of

@@ -171,3 +171,18 @@ def test_random_unmask_shapes(case):
         if not O.near_ties(ref["conf"], mask, S, gamma, min_commit, commit_all):
             break
     run_both(logits, bf16, mask, S, gamma, min_commit=min_commit, commit_all=commit_all, vocab=V)
+
+
+def test_vocabulary_beyond_2_pow_24():
+    """A vocabulary past 2^24 (ragged, padded stride): argmax indices above 2^24 are exact (they
+    travel as integers, never as float32), the lowest of two equal maxima wins up there too."""
+    V = (1 << 24) + 43
+    stride = (V + 7) // 8 * 8
+    rng = np.random.default_rng(24)
+    x = (rng.standard_normal((2, stride), dtype=np.float32) * 3)
+    x[:, V:] = 1e30                      # padding: never read
+    x[0, V - 5] = 30.0                   # maximum in the ragged tail of row 0
+    x[1, (1 << 24) + 7] = 30.0           # a tie above 2^24: the lower index wins
+    x[1, (1 << 24) + 1] = 30.0
+    got, ref = run_both(I.f32_to_bf16_bits(x), True, np.ones(2, np.uint8), 2, 0.9, vocab=V)
+    assert got["argmax"][0] == V - 5 and got["argmax"][1] == (1 << 24) + 1
