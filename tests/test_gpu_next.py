@@ -118,6 +118,25 @@ def test_kv_append_bit_exact(active, shape):
     np.testing.assert_array_equal(ln.cpu().numpy(), rl)
 
 
+def test_kv_append_fills_the_cache_exactly():
+    """The longest sequence's block lands in the last S rows of the cache (max_prefix_len + S equals
+    the capacity); nothing past the cache is written (the tensors are exactly that size)."""
+    w = I.small_workload("append-full", B=2, Hq=8, Hkv=2, D=128, S=16, prefix_len=(100, 300), wid=328)
+    lens = I.prefix_lengths(w)
+    cap = int(lens.max()) + w.S
+    full = I.prefix_cache(w, lens)
+    assert cap <= full["k_cache"].shape[2]
+    cache = {k: np.ascontiguousarray(v[:, :, :cap]) for k, v in full.items()}   # rows past each prefix are 0
+    new = I.attn_inputs(w, lens=lens, cache=False)
+    kc, vc, ln = dev_bf16(cache["k_cache"]), dev_bf16(cache["v_cache"]), dev(lens.copy())
+    bd.kv_append(dev_bf16(new["k_blk"]), dev_bf16(new["v_blk"]), kc, vc, ln, max_prefix_len=int(lens.max()))
+    torch.cuda.synchronize()
+    rk, rv, rl = O.kv_append(cache["k_cache"], cache["v_cache"], lens, new["k_blk"], new["v_blk"])
+    np.testing.assert_array_equal(kc.view(torch.int16).cpu().numpy().view(np.uint16), rk)
+    np.testing.assert_array_equal(vc.view(torch.int16).cpu().numpy().view(np.uint16), rv)
+    np.testing.assert_array_equal(ln.cpu().numpy(), rl)
+
+
 def test_commit_then_next_step_sees_the_appended_block():
     # causal pass + append of block 1, then the next block's denoise-step attention over the grown
     # cache equals the oracle's (its prefix now ends with block 1).
