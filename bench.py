@@ -103,8 +103,9 @@ def row_figures(args, w, bd, torch, dev, recs, steps_used, commits, mask0, lens,
     written), vocab_reduce (the masked rows' logits), commit (latency only). Rows after the step,
     each timed on its own with the same trace (5 launches, first dropped): the context tower's
     causal pass over the block (bd_attn_step, causal), the append of the block to a cache
-    (bd_kv_append), the self-speculation check of a drafted block (bd_spec_verify), and adaptive
-    loop halting (bd_loop_halt) on two hidden states of 32 x 1024 positions x 4096 units, bf16."""
+    (bd_kv_append), the self-speculation check of a drafted block (bd_spec_verify), adaptive
+    loop halting (bd_loop_halt) on two hidden states of 32 x 1024 positions x 4096 units, bf16,
+    and the attention step at the large-batch shape (attn_batched32)."""
     per = {}
     for name, ms in recs:
         per.setdefault(name, []).append(ms)
@@ -201,7 +202,47 @@ def row_figures(args, w, bd, torch, dev, recs, steps_used, commits, mask0, lens,
     rows["loop_halt"] = fig(halt, 2 * hb * hn * 2)
     del h_prev, h_cur
     torch.cuda.synchronize()
+    rows["attn_batched32"] = batched_attention_row(bd, dev)
     return rows
+
+
+def batched_attention_row(bd, dev):
+    """The attention step at the large-batch shape (32 sequences, S = 32, 32q/2kv heads, D = 128,
+    8192-key prefixes: 512 query rows per KV head, MFMA-bound), seeded N(0,1) bf16 inputs drawn on
+    the device, two cache sets alternating; 6 launches with the kernel trace, the first dropped."""
+    import torch
+    from block_diffusion_lm_amd import inputs as I
+    wb = I.WORKLOADS["batched32"]
+    lcap = wb.max_prefix_len
+    g = torch.Generator(device=dev)
+    g.manual_seed(20261204)
+    rnd = lambda *shape: torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+    sets = [(rnd(wb.B, wb.Hkv, lcap, wb.D), rnd(wb.B, wb.Hkv, lcap, wb.D)) for _ in range(2)]
+    q, kb, vb = rnd(wb.B, wb.S, wb.Hq, wb.D), rnd(wb.B, wb.S, wb.Hkv, wb.D), rnd(wb.B, wb.S, wb.Hkv, wb.D)
+    lens = torch.full((wb.B,), lcap, dtype=torch.int32, device=dev)
+    ad = bd.attn_desc(wb.B, wb.Hq, wb.Hkv, wb.D, wb.S, lcap, lcap)
+    ws = torch.empty(max(bd.attn_workspace_bytes(ad), 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    tr = bd.Trace(capacity=64)
+    with tr:
+        for i in range(6):
+            kc, vc = sets[i % 2]
+            bd.attn_step(q, kb, vb, kc, vc, lens, out=out, want_lse=False, max_prefix_len=lcap, workspace=ws)
+    per = {}
+    for name, ms in tr.records():
+        per.setdefault(name, []).append(ms)
+    tr.close()
+    split = float(np.mean(per["attn_split"][1:]))
+    merge = float(np.mean(per["attn_merge"][1:])) if per.get("attn_merge") else 0.0
+    n = lcap + wb.S
+    flops = 4 * wb.B * wb.Hq * wb.S * n * wb.D
+    kvq = wb.B * (2 * wb.Hkv * n * wb.D * 2 + wb.S * wb.Hq * wb.D * 2)
+    tf = flops / (split * 1e-3) / 1e12
+    del sets, q, kb, vb, ws, out
+    torch.cuda.synchronize()
+    return {"workload": "batched32: B=32 Hq=32 Hkv=2 D=128 S=32 L=8192", "split_us": round(split * 1e3, 2),
+            "merge_us": round(merge * 1e3, 2), "tflops": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "gbs": round(kvq / (split * 1e-3) / 1e9, 1), "frac_hbm": round(kvq / (split * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def measured_traffic(kernel_source: str):
