@@ -666,3 +666,17 @@ def test_planted_mistakes_are_caught(monkeypatch):
         rel, halt = orig["loop_halt"](h_prev, h_cur, eps, iteration, max_iter)
         return rel ** 2, halt
     check("loop_halt", halt_squared, [(test_loop_halt_closed_forms_and_library_norm,)])
+
+    # the commit rule's flags and mask: commit_all ignored, the at-least-one fallback dropped,
+    # unmasked positions committed too
+    def no_commit_all(p, a, mask, tokens, S, gamma, min_commit=True, commit_all=False):
+        return orig["commit"](p, a, mask, tokens, S, gamma, min_commit, False)
+    check("commit", no_commit_all, [(test_commit_rule_cases,), (test_gamma_zero_loop_finishes_in_one_step,)])
+
+    def no_fallback(p, a, mask, tokens, S, gamma, min_commit=True, commit_all=False):
+        return orig["commit"](p, a, mask, tokens, S, gamma, False, commit_all)
+    check("commit", no_fallback, [(test_commit_rule_cases,), (test_gamma_zero_and_one,)])
+
+    def ignores_mask(p, a, mask, tokens, S, gamma, min_commit=True, commit_all=False):
+        return orig["commit"](p, a, np.ones_like(mask), tokens, S, gamma, min_commit, commit_all)
+    check("commit", ignores_mask, [(test_commit_rule_cases,), (test_loop_invariants, 0)])
