@@ -243,6 +243,17 @@ def test_vs_library_softmax():
         assert abs(p - float(sm.max())) < 1e-15
 
 
+def test_reduction_is_shift_invariant():
+    # adding a constant to every logit of a row changes neither the argmax nor the softmax maximum
+    # (the maximum is subtracted before exponentiating; +-1000 overflows exp otherwise)
+    row = np.random.default_rng(11).standard_normal(4099) * 4
+    _, a0, _, p0 = O.vocab_reduce(row)
+    for c in (1000.0, -1000.0, 1e6):
+        _, a, _, p = O.vocab_reduce(row + c)
+        assert a == a0
+        assert abs(p - p0) <= 1e-9 * p0
+
+
 def test_argmax_ties_lowest_index():
     row = np.random.default_rng(0).standard_normal(500)
     row[[37, 101, 499]] = 9.0
@@ -677,6 +688,19 @@ def test_planted_mistakes_are_caught(monkeypatch):
         return orig["commit"](p, a, mask, tokens, S, gamma, False, commit_all)
     check("commit", no_fallback, [(test_commit_rule_cases,), (test_gamma_zero_and_one,)])
 
+    def no_shift(row):
+        z = float(np.sum(np.exp(row)))
+        m = float(np.max(row))
+        return m, int(np.flatnonzero(row == m)[0]), z, float(np.exp(m)) / z
+    check("vocab_reduce", no_shift, [(test_reduction_is_shift_invariant,)])
+
     def ignores_mask(p, a, mask, tokens, S, gamma, min_commit=True, commit_all=False):
         return orig["commit"](p, a, np.ones_like(mask), tokens, S, gamma, min_commit, commit_all)
     check("commit", ignores_mask, [(test_commit_rule_cases,), (test_loop_invariants, 0)])
+
+    # the loop commits everything at every step instead of at the last one
+    orig_cu = O.confidence_unmask
+    monkeypatch.setattr(O, "confidence_unmask", lambda *args, **kw: orig_cu(*args, **{**kw, "commit_all": True}))
+    with np.errstate(all="ignore"):
+        assert _fails(test_loop_sequential_decode_with_gamma_one), "no pin caught commit-all at every step"
+    monkeypatch.setattr(O, "confidence_unmask", orig_cu)
