@@ -698,6 +698,20 @@ def test_planted_mistakes_are_caught(monkeypatch):
         return orig["commit"](p, a, np.ones_like(mask), tokens, S, gamma, min_commit, commit_all)
     check("commit", ignores_mask, [(test_commit_rule_cases,), (test_loop_invariants, 0)])
 
+    # a causal mask inside the block in the bidirectional step; sequence 0's cache for every sequence
+    def causal_inside(Qr, K, V, tau, visible=None):
+        if visible is None:
+            S, n = Qr.shape[0], K.shape[0]
+            visible = O.causal_visible(S, n - S, range(S))
+        return orig["softmax_attention"](Qr, K, V, tau, visible)
+    check("softmax_attention", causal_inside, [(test_block_permutation_permutes_outputs,),
+                                               (test_no_prefix_is_plain_bidirectional_attention,)])
+
+    def first_cache(k_blk, v_blk, k_cache, v_cache, prefix_len, b, g):
+        return orig["keys_values"](k_blk, v_blk, k_cache[:1].repeat(k_cache.shape[0], 0),
+                                   v_cache[:1].repeat(v_cache.shape[0], 0), prefix_len, b, g)
+    check("keys_values", first_cache, [(test_tiny_brute_force,)])
+
     # the loop commits everything at every step instead of at the last one
     orig_cu = O.confidence_unmask
     monkeypatch.setattr(O, "confidence_unmask", lambda *args, **kw: orig_cu(*args, **{**kw, "commit_all": True}))
