@@ -6,6 +6,7 @@ no CPU or PyTorch fallback: a missing library raises.
 
     attn_step(q, k_blk, v_blk, k_cache, v_cache, prefix_len, ...)  -> (out, lse)
     confidence_unmask(logits, mask, tokens, block_len, gamma, ...)  -> dict
+    confidence_unmask_noalloc(...)                  the same without a workspace (static scratch)
     denoise_block(get_qkv, get_logits, k_cache, v_cache, prefix_len, mask, tokens, T, ...) -> dict
     attn_step(..., causal=True)                     context-tower pass over a committed block
     kv_append(k_new, v_new, k_cache, v_cache, prefix_len, ...)  prefix-cache append
@@ -20,7 +21,7 @@ from typing import Callable, Optional
 from . import _lib
 from ._lib import AttnDesc, BdError, HaltDesc, StepHooks, UnmaskDesc  # noqa: F401
 
-__all__ = ["attn_step", "confidence_unmask", "denoise_block", "attn_desc", "unmask_desc", "Trace", "BdError",
+__all__ = ["attn_step", "confidence_unmask", "confidence_unmask_noalloc", "denoise_block", "attn_desc", "unmask_desc", "Trace", "BdError",
            "attn_workspace_bytes", "unmask_workspace_bytes", "denoise_workspace_bytes", "version", "kv_append",
            "spec_verify", "loop_halt", "halt_desc", "loop_halt_workspace_bytes"]
 
@@ -236,6 +237,37 @@ def confidence_unmask(logits, mask, tokens, block_len, gamma, vocab=None, min_co
     _lib.check(L.bd_confidence_unmask(ctypes.byref(desc), _ptr(logits), _ptr(mask), _ptr(tokens), _ptr(conf),
                                       _ptr(argmax), _ptr(n_commit), _ptr(ws), ws.numel(), _stream(stream)),
                "bd_confidence_unmask")
+    return {"conf": conf, "argmax": argmax, "n_commit": n_commit}
+
+
+def confidence_unmask_noalloc(logits, mask, tokens, block_len, gamma, vocab=None, min_commit=True,
+                              commit_all=False, outputs=True, stream=None):
+    """bd_confidence_unmask_noalloc on torch tensors: the same operation as confidence_unmask with
+    the library's static per-device scratch instead of a workspace (nothing is allocated by the
+    library; the optional outputs below are the caller's tensors). Returns dict(conf, argmax,
+    n_commit)."""
+    torch = _torch()
+    L = _lib.load()
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("logits must be bfloat16 or float32")
+    _dev_tensor(logits, "logits")
+    _dev_tensor(mask, "mask", torch.uint8)
+    _dev_tensor(tokens, "tokens", torch.int32)
+    rows, stride = logits.shape
+    S = int(block_len)
+    if rows % S != 0 or mask.numel() != rows or tokens.numel() != rows:
+        raise ValueError("logits rows, mask and tokens must all be B*S")
+    B = rows // S
+    V = stride if vocab is None else vocab
+    desc = unmask_desc(B, S, V, stride, logits.dtype == torch.bfloat16, gamma, min_commit, commit_all)
+    conf = argmax = n_commit = None
+    if outputs:
+        conf = torch.empty(rows, dtype=torch.float32, device=logits.device)
+        argmax = torch.empty(rows, dtype=torch.int32, device=logits.device)
+        n_commit = torch.empty(B, dtype=torch.int32, device=logits.device)
+    _lib.check(L.bd_confidence_unmask_noalloc(ctypes.byref(desc), _ptr(logits), _ptr(mask), _ptr(tokens), _ptr(conf),
+                                              _ptr(argmax), _ptr(n_commit), _stream(stream)),
+               "bd_confidence_unmask_noalloc")
     return {"conf": conf, "argmax": argmax, "n_commit": n_commit}
 
 

@@ -72,6 +72,7 @@ EXPORTS = [
     "bd_denoise_workspace_bytes", "bd_denoise_block", "bd_last_error", "bd_trace_create", "bd_trace_destroy",
     "bd_trace_attach", "bd_trace_clear", "bd_trace_count", "bd_trace_get", "bd_version", "bd_table_hooks",
     "bd_kv_append", "bd_spec_verify", "bd_loop_halt_workspace_bytes", "bd_loop_halt",
+    "bd_confidence_unmask_noalloc",
 ]
 
 _lib = None
@@ -117,6 +118,8 @@ def load() -> ctypes.CDLL:
     L.bd_unmask_workspace_bytes.restype = sz
     L.bd_confidence_unmask.argtypes = [P(UnmaskDesc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.bd_confidence_unmask.restype = ctypes.c_int
+    L.bd_confidence_unmask_noalloc.argtypes = [P(UnmaskDesc), vp, vp, vp, vp, vp, vp, vp]
+    L.bd_confidence_unmask_noalloc.restype = ctypes.c_int
     L.bd_denoise_workspace_bytes.argtypes = [P(AttnDesc), P(UnmaskDesc)]
     L.bd_denoise_workspace_bytes.restype = sz
     L.bd_denoise_block.argtypes = [P(AttnDesc), P(UnmaskDesc), i32, i32, P(StepHooks), vp, vp, vp, vp, vp, vp, vp,

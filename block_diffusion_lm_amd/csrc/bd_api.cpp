@@ -362,6 +362,27 @@ bd_status bd_confidence_unmask(const bd_unmask_desc* desc, const void* logits, u
                     nullptr, nullptr, static_cast<hipStream_t>(stream));
 }
 
+bd_status bd_confidence_unmask_noalloc(const bd_unmask_desc* desc, const void* logits, uint8_t* mask,
+                                       int32_t* tokens, float* conf, int32_t* argmax, int32_t* n_commit,
+                                       void* stream) {
+  bd_status st = check_unmask_desc(desc);
+  if (st != BD_OK) return st;
+  st = check_unmask_ptrs(logits, mask, tokens, conf, argmax, n_commit);
+  if (st != BD_OK) return st;
+  bd::UnmaskPlan plan;
+  plan_unmask(desc, &plan);
+  if (plan.bytes > bd::kUnmaskStaticScratchBytes)
+    return fail(BD_EUNSUPPORTED, "bd_confidence_unmask_noalloc: %lld rows need %zu bytes of scratch; the static "
+                "scratch holds %zu (at most %zu rows: use bd_confidence_unmask with a workspace)",
+                (long long)desc->batch * desc->block_len, plan.bytes, bd::kUnmaskStaticScratchBytes,
+                bd::kUnmaskStaticScratchBytes / (3 * sizeof(float)));
+  void* ws = nullptr;
+  const hipError_t e = bd::unmask_static_scratch(&ws);
+  if (e != hipSuccess) return fail(BD_EHIP, "static scratch address: %s", hipGetErrorString(e));
+  return run_unmask(desc, plan, logits, mask, tokens, conf, argmax, n_commit, ws, desc->commit_all, 0, nullptr,
+                    nullptr, static_cast<hipStream_t>(stream));
+}
+
 bd_status bd_kv_append(const bd_attn_desc* desc, const void* k_new, const void* v_new, void* k_cache,
                        void* v_cache, int32_t* prefix_len, const uint8_t* active, void* stream) {
   bd_status st = check_attn_desc(desc);

@@ -112,6 +112,13 @@ struct UnmaskArgs {
 };
 
 hipError_t launch_vocab_reduce(const UnmaskArgs& a, const Launch& l);
+
+// Allocation-free unmasking: the slice partials live in a static device array of this many bytes
+// (one copy per device, held until the process ends) instead of a caller workspace.
+constexpr size_t kUnmaskStaticScratchBytes = (size_t)4 << 20;
+// Device address of the calling thread's current device's copy of that array, resolved with
+// hipGetSymbolAddress on the first call per device and cached.
+hipError_t unmask_static_scratch(void** ptr);
 hipError_t launch_commit(const UnmaskArgs& a, const Launch& l);
 hipError_t launch_spec_accept(const UnmaskArgs& a, const Launch& l);
 hipError_t launch_loop_init(const uint8_t* mask, int B, int S, uint8_t* active, int32_t* steps_used, const Launch& l);

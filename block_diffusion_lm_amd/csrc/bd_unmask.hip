@@ -17,10 +17,20 @@
 // applies the commit rule with ballots: threshold (strict >), or every masked position on the
 // last step, or -- when nothing passes -- the single most confident masked position (lowest
 // position on ties).
+#include <mutex>
+
 #include "bd_internal.h"
 
 namespace bd {
 namespace {
+
+// Scratch of the allocation-free entry point (bd_confidence_unmask_noalloc): the slice partials
+// [B*S][vsplit][3] go here instead of into a caller workspace. Every device that runs the library
+// holds its own copy until the process ends; calls that overlap on one device share it and race.
+// Nothing in it needs clearing: the reduction writes every partial that the commit reads.
+// In host code `scratch` only names the array; its device address comes from
+// unmask_static_scratch() below.
+static __device__ __align__(256) char scratch[kUnmaskStaticScratchBytes];
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -276,6 +286,26 @@ __global__ __launch_bounds__(64) void loop_init_kernel(const uint8_t* mask, int 
 }
 
 }  // namespace
+
+hipError_t unmask_static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_vocab_reduce(const UnmaskArgs& a, const Launch& l) {
   const int64_t blocks = (int64_t)a.B * a.S * a.vsplit;

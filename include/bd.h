@@ -178,6 +178,18 @@ bd_status bd_confidence_unmask(const bd_unmask_desc* desc, const void* logits,
                                float* conf, int32_t* argmax, int32_t* n_commit,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same operation with no workspace and no allocation of any kind, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc). The slice partials live in a static scratch array inside the library: 4 MiB per
+ * device, held until the process ends, which bounds the problem to B*S <= 349525 rows (larger
+ * descriptors return BD_EUNSUPPORTED before anything is enqueued). The first call on a device
+ * resolves that array's address (hipGetSymbolAddress); make it once outside any capture. Calls
+ * that overlap on one device share the array and race: serialise them (one stream, or events).
+ * Arguments and results otherwise exactly as bd_confidence_unmask. */
+bd_status bd_confidence_unmask_noalloc(const bd_unmask_desc* desc, const void* logits,
+                                       uint8_t* mask, int32_t* tokens,
+                                       float* conf, int32_t* argmax, int32_t* n_commit, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * Self-speculation check (LinearSpec): commit the prefix of a drafted block that AR decoding
  * would produce

@@ -144,6 +144,26 @@ def test_unmask_pointer_validation(L):
     assert L.bd_confidence_unmask(ctypes.byref(d), p, p, p, None, None, None, p, nb - 1, None) == _lib.BD_EWORKSPACE
 
 
+def test_unmask_noalloc_host_checks(L):
+    """The allocation-free unmasking validates like bd_confidence_unmask and rejects, before any
+    device call, problems whose slice partials exceed its 4 MiB static scratch (B*S > 349525)."""
+    p = ctypes.c_void_p(4096)
+    d = good_unmask()
+    d.gamma = 2.0
+    assert L.bd_confidence_unmask_noalloc(ctypes.byref(d), p, p, p, None, None, None, None) == _lib.BD_EINVAL
+    d = good_unmask()
+    assert L.bd_confidence_unmask_noalloc(ctypes.byref(d), None, p, p, None, None, None, None) == _lib.BD_EINVAL
+    assert L.bd_confidence_unmask_noalloc(ctypes.byref(d), p, p, None, None, None, None, None) == _lib.BD_EINVAL
+    big = _lib.UnmaskDesc(5462, 64, 4096, 4096, _lib.BD_F32, 0.9, 1, 0)     # 349568 rows
+    assert L.bd_confidence_unmask_noalloc(ctypes.byref(big), p, p, p, None, None, None, None) == _lib.BD_EUNSUPPORTED
+    assert b"static scratch" in L.bd_last_error()
+    # the largest accepted problem fills the scratch exactly: its workspace query is 4 MiB
+    edge = _lib.UnmaskDesc(349525, 1, 4096, 4096, _lib.BD_F32, 0.9, 1, 0)
+    assert L.bd_unmask_workspace_bytes(ctypes.byref(edge)) == 4 << 20
+    edge.batch += 1
+    assert L.bd_unmask_workspace_bytes(ctypes.byref(edge)) > 4 << 20
+
+
 def test_denoise_validation(L):
     ad = good_attn()
     ud = good_unmask()
