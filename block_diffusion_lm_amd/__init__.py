@@ -21,7 +21,7 @@ from typing import Callable, Optional
 from . import _lib
 from ._lib import AttnDesc, BdError, HaltDesc, StepHooks, UnmaskDesc  # noqa: F401
 
-__all__ = ["attn_step", "confidence_unmask", "confidence_unmask_noalloc", "denoise_block", "attn_desc", "unmask_desc", "Trace", "BdError",
+__all__ = ["attn_step", "attn_plan", "confidence_unmask", "confidence_unmask_noalloc", "denoise_block", "attn_desc", "unmask_desc", "Trace", "BdError",
            "attn_workspace_bytes", "unmask_workspace_bytes", "denoise_workspace_bytes", "version", "kv_append",
            "spec_verify", "loop_halt", "halt_desc", "loop_halt_workspace_bytes"]
 
@@ -66,6 +66,13 @@ def attn_desc(B, Hq, Hkv, D, S, prefix_capacity, max_prefix_len=None, softmax_sc
 def unmask_desc(B, S, V, row_stride=None, bf16=True, gamma=0.9, min_commit=True, commit_all=False) -> UnmaskDesc:
     return UnmaskDesc(B, S, V, V if row_stride is None else row_stride, _lib.BD_BF16 if bf16 else _lib.BD_F32,
                       gamma, int(bool(min_commit)), int(bool(commit_all)))
+
+
+def attn_plan(desc: AttnDesc) -> dict:
+    """bd_attn_plan: how bd_attn_step runs this descriptor (work-group shape, row tiles, chunks)."""
+    info = _lib.AttnPlanInfo()
+    _lib.check(_lib.load().bd_attn_plan(ctypes.byref(desc), ctypes.byref(info)), "bd_attn_plan")
+    return {f: int(getattr(info, f)) for f, _ in _lib.AttnPlanInfo._fields_}
 
 
 def attn_workspace_bytes(desc: AttnDesc) -> int:

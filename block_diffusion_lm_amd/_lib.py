@@ -27,6 +27,17 @@ class AttnDesc(ctypes.Structure):
     ]
 
 
+class AttnPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("waves", ctypes.c_int32),
+        ("rows_per_wave", ctypes.c_int32),
+        ("row_tiles", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("chunk_keys", ctypes.c_int64),
+        ("workgroups", ctypes.c_int64),
+    ]
+
+
 class UnmaskDesc(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32),
@@ -72,7 +83,7 @@ EXPORTS = [
     "bd_denoise_workspace_bytes", "bd_denoise_block", "bd_last_error", "bd_trace_create", "bd_trace_destroy",
     "bd_trace_attach", "bd_trace_clear", "bd_trace_count", "bd_trace_get", "bd_version", "bd_table_hooks",
     "bd_kv_append", "bd_spec_verify", "bd_loop_halt_workspace_bytes", "bd_loop_halt",
-    "bd_confidence_unmask_noalloc",
+    "bd_confidence_unmask_noalloc", "bd_attn_plan",
 ]
 
 _lib = None
@@ -118,6 +129,8 @@ def load() -> ctypes.CDLL:
     L.bd_unmask_workspace_bytes.restype = sz
     L.bd_confidence_unmask.argtypes = [P(UnmaskDesc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.bd_confidence_unmask.restype = ctypes.c_int
+    L.bd_attn_plan.argtypes = [P(AttnDesc), P(AttnPlanInfo)]
+    L.bd_attn_plan.restype = ctypes.c_int
     L.bd_confidence_unmask_noalloc.argtypes = [P(UnmaskDesc), vp, vp, vp, vp, vp, vp, vp]
     L.bd_confidence_unmask_noalloc.restype = ctypes.c_int
     L.bd_denoise_workspace_bytes.argtypes = [P(AttnDesc), P(UnmaskDesc)]

@@ -325,6 +325,21 @@ size_t bd_attn_workspace_bytes(const bd_attn_desc* desc) {
   return p.bytes;
 }
 
+bd_status bd_attn_plan(const bd_attn_desc* desc, bd_attn_plan_info* info) {
+  bd_status st = check_attn_desc(desc);
+  if (st != BD_OK) return st;
+  if (!info) return fail(BD_EINVAL, "info is NULL");
+  bd::AttnPlan p;
+  plan_attn(desc, &p);
+  info->waves = p.waves;
+  info->rows_per_wave = p.rows_per_wave;
+  info->row_tiles = p.row_tiles;
+  info->num_splits = p.nsplit;
+  info->chunk_keys = p.chunk;
+  info->workgroups = p.n_items;
+  return BD_OK;
+}
+
 bd_status bd_attn_step(const bd_attn_desc* desc, const void* q, const void* k_blk, const void* v_blk,
                        const void* k_cache, const void* v_cache, const int32_t* prefix_len, const uint8_t* active,
                        void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {

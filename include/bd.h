@@ -104,6 +104,20 @@ typedef struct {
 /* Workspace bytes bd_attn_step needs for this descriptor (0 on an invalid descriptor). */
 size_t bd_attn_workspace_bytes(const bd_attn_desc* desc);
 
+/* How bd_attn_step will run a descriptor (host-side query; nothing is enqueued): work-group shape,
+ * row tiles and key chunks per (sequence, KV head). For diagnostics and tests. */
+typedef struct {
+  int32_t waves;            /* waves (of 64 lanes) per work-group */
+  int32_t rows_per_wave;    /* query rows a wave owns (32-row MFMA blocks x 32) */
+  int32_t row_tiles;        /* work-groups per (sequence, KV head, chunk) along the query rows */
+  int32_t num_splits;       /* key chunks per (sequence, KV head) */
+  int64_t chunk_keys;       /* keys per chunk (a multiple of 64) */
+  int64_t workgroups;       /* work-groups of the split launch */
+} bd_attn_plan_info;
+
+/* BD_OK and *info filled (host pointer), or the descriptor's validation error. */
+bd_status bd_attn_plan(const bd_attn_desc* desc, bd_attn_plan_info* info);
+
 /* q:        bf16 [B, S, Hq, D]            (read only)
  * k_blk:    bf16 [B, S, Hkv, D]           (read only)  keys of the active block
  * v_blk:    bf16 [B, S, Hkv, D]           (read only)

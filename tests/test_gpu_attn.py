@@ -2,9 +2,9 @@
 
 Small shapes (whole tensors compared) span several key tiles, several splits, ragged tails,
 padded row tiles, S = 1 (AR decode), L = 0 and head_dim 64/128. The official workloads run at
-full size in the launch configuration the benchmark uses, checked on sampled rows the oracle
-computes one by one, plus properties that hold at any size (determinism, the cache is never
-written, inactive sequences untouched, canaries around the output intact)."""
+full size in the launch configuration the benchmark uses, every output element compared with the
+oracle, plus properties that hold at any size (determinism, the cache is never written, inactive
+sequences untouched, canaries around the output intact)."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +12,8 @@ import torch
 import block_diffusion_lm_amd as bd
 from block_diffusion_lm_amd import inputs as I
 from oracle import bd_oracle as O
-from tests.gpu_util import LSE_ATOL, assert_attn_close, bf16_f64, dev, dev_bf16, guarded, guards_intact, host_f64
+from tests.gpu_util import (LSE_ATOL, assert_attn_close, bf16_f64, dev, dev_bf16, guarded, guards_intact, host_f64,
+                             oracle_attn_all)
 
 pytestmark = pytest.mark.gpu
 
@@ -125,29 +126,20 @@ def test_inactive_sequences_and_canaries():
         assert_attn_close(got, ref[[0, 2]], "active")
 
 
-def sampled_rows(w, lens, n=24, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = {(0, 0, 0), (w.B - 1, w.S - 1, w.Hq - 1), (0, w.S - 1, w.Hq // 2), (w.B - 1, 0, 1)}
-    while len(rows) < n:
-        rows.add((int(rng.integers(w.B)), int(rng.integers(w.S)), int(rng.integers(w.Hq))))
-    return sorted(rows)
-
-
 @pytest.mark.parametrize("name", ["decode", "batched16", "batched32", "long", "stress_a", "stress_b"])
-def test_official_workloads_full_size_sampled(name):
+def test_official_workloads_full_size(name):
+    """Every element of out and lse at full size, in the launch configuration the benchmark uses,
+    against the oracle computed row by row (one (sequence, KV head) slab at a time)."""
     w = I.WORKLOADS[name]
     print(f"[attn] full-size {name}", flush=True)
     inp = I.attn_inputs(w)
     got, lse, t = run_gpu(inp)
-    rows = sampled_rows(w, inp["prefix_len"], n=48 if name == "decode" else 24)
-    ref = O.attn_rows(inp["q"], inp["k_blk"], inp["v_blk"], inp["k_cache"], inp["v_cache"], inp["prefix_len"], rows)
-    g = np.stack([got[b, s, h] for (b, s, h) in rows])
-    r = np.stack([ref[k][0] for k in rows])
-    assert_attn_close(g, r, name)
-    np.testing.assert_allclose([lse[b, h, s] for (b, s, h) in rows], [ref[k][1] for k in rows], rtol=0, atol=LSE_ATOL)
-    # the whole output is finite and the cache was not written
-    assert np.all(np.isfinite(got))
+    ref, ref_lse = oracle_attn_all(inp)
+    assert_attn_close(got, ref, name)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
+    # the cache was not written
     assert torch.equal(t["k_cache"].view(torch.int16).cpu(), torch.from_numpy(inp["k_cache"].view(np.int16)))
+    assert torch.equal(t["v_cache"].view(torch.int16).cpu(), torch.from_numpy(inp["v_cache"].view(np.int16)))
 
 
 EDGE = [
@@ -175,6 +167,33 @@ def test_tile_edge_lengths(case, num_splits, causal):
     ref, ref_lse = O.attn_step(f["q"], f["k_blk"], f["v_blk"], f["k_cache"], f["v_cache"], inp["prefix_len"],
                                causal=causal)
     assert_attn_close(got, ref, name)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
+
+
+WIDE_EDGE_LENS = [(4096, 4097), (4031, 4161), (4095, 4160), (4159, 4033), (4032, 4096)]
+
+
+@pytest.mark.parametrize("lens", WIDE_EDGE_LENS, ids=[f"L{a}-{b}" for a, b in WIDE_EDGE_LENS])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_tile_edges_of_the_long_prefix_kernel(lens, D, num_splits, causal):
+    """Tile-edge prefix lengths (a multiple of 64 keys and +-1 around it) in shapes that plan the
+    long-prefix kernel -- one 256-row work-group per (sequence, KV head, chunk), the launch the
+    long, batched and stress workloads use -- asserted through the plan query so a planner change
+    cannot silently move these cases to another kernel. Both modes, both head dims, forced splits."""
+    lens = np.asarray(lens, np.int32)
+    w = I.small_workload(f"wide-edge-{D}", B=2, Hq=128, Hkv=8, D=D, S=16, prefix_len=int(lens.max()),
+                         wid=330 + D // 64)
+    desc = bd.attn_desc(w.B, w.Hq, w.Hkv, w.D, w.S, int(lens.max()), int(lens.max()), num_splits=num_splits,
+                        causal=causal)
+    plan = bd.attn_plan(desc)
+    assert plan["waves"] * plan["rows_per_wave"] == 256 and plan["row_tiles"] == 1, plan
+    inp = I.attn_inputs(w, lens=lens)
+    print(f"[attn] wide-edge D={D} splits={num_splits} causal={causal} lens={lens.tolist()} plan={plan}", flush=True)
+    got, lse, _ = run_gpu(inp, num_splits=num_splits, causal=causal)
+    ref, ref_lse = oracle_attn_all(inp, causal=causal)
+    assert_attn_close(got, ref, f"wide-edge-{D}")
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
 
 

@@ -11,12 +11,12 @@ import torch
 import block_diffusion_lm_amd as bd
 from block_diffusion_lm_amd import inputs as I
 from oracle import bd_oracle as O
-from tests.gpu_util import assert_attn_close, bf16_f64, dev, dev_bf16, host_f64
+from tests.gpu_util import assert_attn_close, bf16_f64, dev, dev_bf16, host_f64, oracle_attn_all
 
 pytestmark = pytest.mark.gpu
 
 
-def run_loop(w, t0=0, mask0=None, tokens0=None, T=None, full_oracle=True, sample_rows=None):
+def run_loop(w, t0=0, mask0=None, tokens0=None, T=None, full_oracle=True):
     T = w.T if T is None else T
     lens = I.prefix_lengths(w)
     cache = I.prefix_cache(w, lens)
@@ -55,7 +55,8 @@ def run_loop(w, t0=0, mask0=None, tokens0=None, T=None, full_oracle=True, sample
                               lens, w.gamma, bool(w.min_commit), True,
                               logits_decode=O.bf16_to_f64 if is_bf16 else None)
     else:
-        # control flow only (the logits do not depend on the attention): attention sampled below
+        # control flow only (the logits do not depend on the attention); every row of every
+        # executed step's attention is checked below, one (sequence, KV head) slab at a time
         mask, tokens = mask0.copy(), tokens0.copy()
         ref = {"steps_used": np.zeros(w.B, np.int32), "commits": np.zeros((T, w.B), np.int32), "active": {},
                "masks": {}}
@@ -84,10 +85,9 @@ def run_loop(w, t0=0, mask0=None, tokens0=None, T=None, full_oracle=True, sample
         if full_oracle:
             assert_attn_close(got[act], ref["outs"][t][act], f"step {t}")
         else:
-            rows = sample_rows(t, act)
-            r = O.attn_rows(steps[t]["q"], steps[t]["k_blk"], steps[t]["v_blk"], cache["k_cache"], cache["v_cache"],
-                            lens, rows)
-            assert_attn_close(np.stack([got[k] for k in rows]), np.stack([r[k][0] for k in rows]), f"step {t}")
+            step_inp = dict(steps[t], k_cache=cache["k_cache"], v_cache=cache["v_cache"], prefix_len=lens)
+            ref_o, _ = oracle_attn_all(step_inp, active=act)
+            assert_attn_close(got[act], ref_o[act], f"step {t}")
     return res, ref
 
 
@@ -107,13 +107,7 @@ def test_loop_resume_from_t0():
 
 def test_long_workload_full_loop():
     w = I.WORKLOADS["long"]
-    rng = np.random.default_rng(1)
-
-    def rows(t, act):
-        bs = np.flatnonzero(act)
-        return sorted({(int(rng.choice(bs)), int(rng.integers(w.S)), int(rng.integers(w.Hq))) for _ in range(6)})
-
-    res, ref = run_loop(w, full_oracle=False, sample_rows=rows)
+    res, ref = run_loop(w, full_oracle=False)
     assert ref["steps_used"].max() >= 2      # the loop runs several steps before every position commits
 
 

@@ -10,7 +10,7 @@ import torch
 import block_diffusion_lm_amd as bd
 from block_diffusion_lm_amd import inputs as I
 from oracle import bd_oracle as O
-from tests.gpu_util import LSE_ATOL, assert_attn_close, bf16_f64, dev, dev_bf16, host_f64
+from tests.gpu_util import LSE_ATOL, assert_attn_close, bf16_f64, dev, dev_bf16, host_f64, oracle_attn_all
 
 pytestmark = pytest.mark.gpu
 
@@ -65,16 +65,18 @@ def test_causal_last_row_equals_bidirectional_and_first_rows_differ():
     assert np.abs(gc[:, 0] - gb[:, 0]).max() > 1e-3
 
 
-def test_causal_full_size_sampled():
-    # the decode workload's shape (32q/2kv, D128, S16, L4096) in causal mode, sampled rows
-    w = I.WORKLOADS["decode"]
+@pytest.mark.parametrize("name", ["decode", "long"])
+def test_causal_full_size(name):
+    """The context tower's pass at full size (the decode and long workloads' shapes in causal mode):
+    every element of out and lse against the oracle."""
+    w = I.WORKLOADS[name]
     lens = I.prefix_lengths(w)
     inp = I.attn_inputs(w, lens=lens)
-    got, _ = run_attn(inp, causal=True)
-    rng = np.random.default_rng(3)
-    rows = sorted({(0, int(rng.integers(w.S)), int(rng.integers(w.Hq))) for _ in range(12)} | {(0, 0, 0), (0, 15, 31)})
-    ref = O.attn_rows(inp["q"], inp["k_blk"], inp["v_blk"], inp["k_cache"], inp["v_cache"], lens, rows, causal=True)
-    assert_attn_close(np.stack([got[k] for k in rows]), np.stack([ref[k][0] for k in rows]), "decode causal")
+    print(f"[causal] full-size {name}", flush=True)
+    got, lse = run_attn(inp, causal=True)
+    ref, ref_lse = oracle_attn_all(inp, causal=True)
+    assert_attn_close(got, ref, f"{name} causal")
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
 
 
 def capacity_cache(w, lens, extra):

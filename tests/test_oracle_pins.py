@@ -202,6 +202,27 @@ def test_sampled_rows_match_full():
         assert abs(got[(b, s, h)][1] - Lo[b, h, s]) < 1e-12
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_on_bf16_bits_match_decoded_full(D, causal):
+    """attn_rows' bf16 branch (uint16 bit patterns decoded one (sequence, KV head) slab at a time,
+    as the full-size GPU checks use it) gives the rows of attn_step run on the whole decoded
+    tensors: every (b, s, h), ragged prefix lengths including 0, both attention modes."""
+    from block_diffusion_lm_amd import inputs as I
+    w = I.small_workload("rows-bits", B=3, Hq=8, Hkv=2, D=D, S=5, prefix_len=70, wid=900 + D + int(causal))
+    lens = np.array([70, 0, 33], np.int32)
+    inp = I.attn_inputs(w, lens=lens)
+    assert inp["q"].dtype == np.uint16
+    f = {k: O.bf16_to_f64(inp[k]) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
+    Oo, Lo = O.attn_step(f["q"], f["k_blk"], f["v_blk"], f["k_cache"], f["v_cache"], lens, causal=causal)
+    rows = [(b, s, h) for b in range(3) for s in range(5) for h in range(8)]
+    got = O.attn_rows(inp["q"], inp["k_blk"], inp["v_blk"], inp["k_cache"], inp["v_cache"], lens, rows, causal=causal)
+    assert set(got) == set(rows)
+    for (b, s, h) in rows:
+        np.testing.assert_allclose(got[(b, s, h)][0], Oo[b, s, h], rtol=1e-12, atol=1e-14)
+        assert abs(got[(b, s, h)][1] - Lo[b, h, s]) < 1e-12
+
+
 def test_inactive_sequences_are_skipped():
     q, kb, vb, kc, vc, lens = make_case(B=2, S=2, Hq=2, Hkv=1, D=4, lens=(3, 3), seed=2)
     Oo, _ = O.attn_step(q, kb, vb, kc, vc, lens, active=[1, 0])
