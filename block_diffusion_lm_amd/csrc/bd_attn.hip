@@ -96,26 +96,83 @@ __device__ __forceinline__ ItemMap device_plan(const AttnArgs& a, int n_act) {
   return m;
 }
 
-// Number of active sequences, the sequence index of the i-th active one, and the rank of an
-// active sequence among them.
-__device__ __forceinline__ int count_active(const uint8_t* active, int B) {
-  if (!active) return B;
-  int n = 0;
-  for (int i = 0; i < B; ++i) n += active[i] != 0;
-  return n;
-}
-__device__ __forceinline__ int nth_active(const uint8_t* active, int B, int i) {
-  if (!active) return i;
-  for (int b = 0; b < B; ++b)
-    if (active[b] && i-- == 0) return b;
-  return 0;
-}
-__device__ __forceinline__ int rank_active(const uint8_t* active, int b) {
-  if (!active) return b;
-  int r = 0;
-  for (int i = 0; i < b; ++i) r += active[i] != 0;
-  return r;
-}
+// Active-sequence bookkeeping, shared by a work-group of NT threads: the active flags are scanned
+// NT at a time (ceil(B / NT) rounds); every round turns each wave's 64 flags into a ballot mask in
+// LDS, from which counts and ranks follow by population counts. All threads take part (the rounds
+// hold barriers); the results are uniform across the work-group.
+template <int NT>
+struct ActiveScan {
+  static constexpr int NWV = NT / 64;
+  uint64_t* masks;   // NWV masks in LDS
+  __device__ void load(const uint8_t* active, int B, int base) {
+    const int idx = base + (int)threadIdx.x;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(idx < B && active[idx] != 0);
+    if ((threadIdx.x & 63) == 0) masks[threadIdx.x >> 6] = m;
+    __syncthreads();
+  }
+  __device__ int chunk_count() const {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) c += __popcll(masks[w]);
+    return c;
+  }
+  // active flags before offset `off` of the loaded chunk
+  __device__ int rank_in_chunk(int off) const {
+    int r = 0;
+    for (int w = 0; w < off / 64; ++w) r += __popcll(masks[w]);
+    const int l = off % 64;
+    return r + (l ? __popcll(masks[off / 64] & ((~0ull) >> (64 - l))) : 0);
+  }
+  // offset in the loaded chunk of its k-th active flag (0 <= k < chunk_count())
+  __device__ int select_in_chunk(int k) const {
+    for (int w = 0; w < NWV; ++w) {
+      uint64_t m = masks[w];
+      const int c = __popcll(m);
+      if (k < c) {
+        for (int j = 0; j < k; ++j) m &= m - 1;   // drop the k lowest set bits
+        return w * 64 + __builtin_ctzll(m);
+      }
+      k -= c;
+    }
+    return 0;
+  }
+  // number of active sequences (B without a mask)
+  __device__ int count(const uint8_t* active, int B) {
+    if (!active) return B;
+    int n = 0;
+    for (int base = 0; base < B; base += NT) {
+      load(active, B, base);
+      n += chunk_count();
+      __syncthreads();
+    }
+    return n;
+  }
+  // the sequence of active rank i
+  __device__ int nth(const uint8_t* active, int B, int i) {
+    if (!active) return i;
+    int before = 0, found = 0;
+    for (int base = 0; base < B; base += NT) {
+      load(active, B, base);
+      const int c = chunk_count();
+      if (i >= before && i < before + c) found = base + select_in_chunk(i - before);
+      before += c;
+      __syncthreads();
+    }
+    return found;
+  }
+  // the rank of sequence b among the active ones (b's flag need not be set)
+  __device__ int rank(const uint8_t* active, int B, int b) {
+    if (!active) return b;
+    int r = 0;
+    for (int base = 0; base < B; base += NT) {
+      load(active, B, base);
+      if (b >= base + NT) r += chunk_count();
+      else if (b >= base) r += rank_in_chunk(b - base);
+      __syncthreads();
+    }
+    return r;
+  }
+};
 
 template <int D>
 struct Geo {
@@ -257,14 +314,16 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
   if ((nitems & 7) == 0) item = (item & 7) * (nitems >> 3) + (item >> 3);
   // (values loaded from memory are made explicitly wave-uniform, so that the tile bookkeeping
   // and the DMA bases below live in scalar registers)
-  const int n_act = __builtin_amdgcn_readfirstlane(count_active(a.active, a.B));
+  __shared__ uint64_t act_masks[NW];
+  ActiveScan<NT> scan{act_masks};
+  const int n_act = __builtin_amdgcn_readfirstlane(scan.count(a.active, a.B));
   const ItemMap im = device_plan(a, n_act);
   const int rt = (int)(item % a.row_tiles);
   const int64_t ps = item / a.row_tiles;
   const int split = (int)(ps % im.nsplit);
   const int64_t pair_a = ps / im.nsplit;              // pair among the active sequences
   if (pair_a >= (int64_t)n_act * a.Hkv) return;
-  const int b = __builtin_amdgcn_readfirstlane(nth_active(a.active, a.B, (int)(pair_a / a.Hkv)));
+  const int b = __builtin_amdgcn_readfirstlane(scan.nth(a.active, a.B, (int)(pair_a / a.Hkv)));
   const int g = (int)(pair_a % a.Hkv);
   const int64_t len = __builtin_amdgcn_readfirstlane(a.prefix_len[b]);
   const int64_t nkeys = len + a.S;
@@ -769,13 +828,17 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int tile_ro
   const int b = pair / a.Hkv;
   const int g = pair % a.Hkv;
   const bool act = live && !(a.active && !a.active[b]);
-  const int n_act = count_active(a.active, a.B);
+  __shared__ uint64_t act_masks[4];
+  ActiveScan<256> scan{act_masks};
+  const int n_act = scan.count(a.active, a.B);
   const ItemMap im = device_plan(a, n_act);
   if (im.nsplit == 1) return;   // the split kernel wrote the output itself
+  // ranks of this thread's sequence (every thread takes part in the scan's barriers)
+  const int rank_b = scan.rank(a.active, a.B, b);
   int ns = 0;
   int64_t p0 = 0, pstride = 0;
   if (act) {
-    const int64_t pair_a = (int64_t)rank_active(a.active, b) * a.Hkv + g;
+    const int64_t pair_a = (int64_t)rank_b * a.Hkv + g;
     const int64_t nkeys = (int64_t)a.prefix_len[b] + a.S;
     ns = (int)min((int64_t)im.nsplit, (nkeys + im.chunk - 1) / im.chunk);
     const int rt = r / tile_rows;

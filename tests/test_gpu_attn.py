@@ -197,6 +197,46 @@ def test_tile_edges_of_the_long_prefix_kernel(lens, D, num_splits, causal):
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
 
 
+MANY = [
+    # name, Hq, Hkv, D, num_splits: 512 sequences; 64 rows per KV head plans the four-wave kernel,
+    # 256 rows the eight-wave one; forced splits run the merge and the device re-plan over the
+    # active sequences
+    ("many-4w", 8, 2, 64, 0),
+    ("many-8w", 32, 2, 128, 0),
+    ("many-8w-split3", 32, 2, 128, 3),
+]
+
+
+@pytest.mark.parametrize("case", MANY, ids=[c[0] for c in MANY])
+def test_many_sequences_with_a_ragged_active_mask(case):
+    """512 sequences, a seeded ragged active mask (first inactive, last active): the work-groups
+    find their sequence and the merge its partial rows through the work-group scan of the flags.
+    Active rows match the oracle; inactive rows keep the canary fill."""
+    name, Hq, Hkv, D, num_splits = case
+    B = 512
+    w = I.small_workload(name, B=B, Hq=Hq, Hkv=Hkv, D=D, S=16, prefix_len=(60, 700), wid=340 + MANY.index(case))
+    inp = I.attn_inputs(w)
+    act = (np.random.default_rng(341).random(B) < 0.45).astype(np.uint8)
+    act[0], act[-1] = 0, 1
+    plan = bd.attn_plan(bd.attn_desc(B, Hq, Hkv, D, 16, inp["k_cache"].shape[2], int(inp["prefix_len"].max()),
+                                     num_splits=num_splits))
+    assert plan["waves"] == (8 if Hq == 32 else 4), plan
+    print(f"[attn] {name} active={int(act.sum())} plan={plan}", flush=True)
+    t = {k: dev_bf16(inp[k]) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
+    big, out, gd = guarded(tuple(inp["q"].shape), torch.bfloat16)
+    b0 = big.clone()
+    bd.attn_step(t["q"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], dev(inp["prefix_len"]), active=dev(act),
+                 out=out, want_lse=False, num_splits=num_splits, max_prefix_len=int(inp["prefix_len"].max()))
+    torch.cuda.synchronize()
+    assert guards_intact(big, gd, out.numel(), b0)
+    keep = b0[gd:gd + out.numel()].view(out.shape)
+    ina = torch.from_numpy(act == 0).cuda()
+    assert torch.equal(out[ina].view(torch.int16), keep[ina].view(torch.int16))
+    got = host_f64(out[torch.from_numpy(act == 1).cuda()])
+    ref, _ = oracle_attn_all(inp, active=act)
+    assert_attn_close(got, ref[act == 1], name)
+
+
 @pytest.mark.parametrize("num_splits", [0, 1, 3])
 def test_largest_query_group(num_splits):
     """The largest row count per KV head the descriptor allows in one group: S = 64 block positions
