@@ -103,9 +103,8 @@ def row_figures(args, w, bd, torch, dev, recs, steps_used, commits, mask0, lens,
     written), vocab_reduce (the masked rows' logits), commit (latency only). Rows after the step,
     each timed on its own with the same trace (5 launches, first dropped): the context tower's
     causal pass over the block (bd_attn_step, causal), the append of the block to a cache
-    (bd_kv_append), the self-speculation check of a drafted block (bd_spec_verify), adaptive
-    loop halting (bd_loop_halt) on two hidden states of 32 x 1024 positions x 4096 units, bf16,
-    and the attention step at the large-batch shape (attn_batched32)."""
+    (bd_kv_append), the self-speculation check of a drafted block (bd_spec_verify) and adaptive
+    loop halting (bd_loop_halt) on two hidden states of 32 x 1024 positions x 4096 units, bf16."""
     per = {}
     for name, ms in recs:
         per.setdefault(name, []).append(ms)
@@ -202,47 +201,92 @@ def row_figures(args, w, bd, torch, dev, recs, steps_used, commits, mask0, lens,
     rows["loop_halt"] = fig(halt, 2 * hb * hn * 2)
     del h_prev, h_cur
     torch.cuda.synchronize()
-    rows["attn_batched32"] = batched_attention_row(bd, dev)
     return rows
 
 
-def batched_attention_row(bd, dev):
-    """The attention step at the large-batch shape (32 sequences, S = 32, 32q/2kv heads, D = 128,
-    8192-key prefixes: 512 query rows per KV head, MFMA-bound), seeded N(0,1) bf16 inputs drawn on
-    the device, two cache sets alternating; 6 launches with the kernel trace, the first dropped."""
+def config_rows(bd, dev):
+    """One row per workload besides the loop's: the attention step (split + merge kernels) and the
+    confidence unmasking (vocabulary reduction + commit kernels) at full size -- single-sequence
+    decode (L 4096), the batched step at S = 16 and S = 32 (32 sequences, L 8192), one 262144-token
+    prefix, and the ragged batch (16 sequences, 8 KV heads, the workload's seeded lengths in
+    [1024, 32768]). Attention inputs are seeded N(0,1) bf16 and logits N(0,3) bf16 drawn on the
+    device (the workload's shapes, lengths and masked positions); three independent cache and
+    logits sets rotate so consecutive launches do not find their bytes in the 256 MB Infinity
+    Cache. 7 launches of each with the kernel trace, the first dropped.
+
+    Attention: TFLOP/s and K/V/Q GB/s over split + merge, with their fractions of the dense bf16
+    MFMA peak and of HBM; unmask: masked positions per second over reduction + commit, against the
+    HBM roofline 8e12 / (V * 2) positions/s."""
     import torch
     from block_diffusion_lm_amd import inputs as I
-    wb = I.WORKLOADS["batched32"]
-    lcap = wb.max_prefix_len
+    out_rows = {}
     g = torch.Generator(device=dev)
-    g.manual_seed(20261204)
-    rnd = lambda *shape: torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
-    sets = [(rnd(wb.B, wb.Hkv, lcap, wb.D), rnd(wb.B, wb.Hkv, lcap, wb.D)) for _ in range(2)]
-    q, kb, vb = rnd(wb.B, wb.S, wb.Hq, wb.D), rnd(wb.B, wb.S, wb.Hkv, wb.D), rnd(wb.B, wb.S, wb.Hkv, wb.D)
-    lens = torch.full((wb.B,), lcap, dtype=torch.int32, device=dev)
-    ad = bd.attn_desc(wb.B, wb.Hq, wb.Hkv, wb.D, wb.S, lcap, lcap)
-    ws = torch.empty(max(bd.attn_workspace_bytes(ad), 1), dtype=torch.uint8, device=dev)
-    out = torch.empty_like(q)
-    tr = bd.Trace(capacity=64)
-    with tr:
-        for i in range(6):
-            kc, vc = sets[i % 2]
-            bd.attn_step(q, kb, vb, kc, vc, lens, out=out, want_lse=False, max_prefix_len=lcap, workspace=ws)
-    per = {}
-    for name, ms in tr.records():
-        per.setdefault(name, []).append(ms)
-    tr.close()
-    split = float(np.mean(per["attn_split"][1:]))
-    merge = float(np.mean(per["attn_merge"][1:])) if per.get("attn_merge") else 0.0
-    n = lcap + wb.S
-    flops = 4 * wb.B * wb.Hq * wb.S * n * wb.D
-    kvq = wb.B * (2 * wb.Hkv * n * wb.D * 2 + wb.S * wb.Hq * wb.D * 2)
-    tf = flops / (split * 1e-3) / 1e12
-    del sets, q, kb, vb, ws, out
-    torch.cuda.synchronize()
-    return {"workload": "batched32: B=32 Hq=32 Hkv=2 D=128 S=32 L=8192", "split_us": round(split * 1e3, 2),
-            "merge_us": round(merge * 1e3, 2), "tflops": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
-            "gbs": round(kvq / (split * 1e-3) / 1e9, 1), "frac_hbm": round(kvq / (split * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    g.manual_seed(20261205)
+    for name in ("decode", "batched16", "batched32", "stress_a", "stress_b"):
+        w = I.WORKLOADS[name]
+        print(f"[bench] row {name}", file=sys.stderr, flush=True)
+        lens_np = I.prefix_lengths(w)
+        lcap = int(lens_np.max())
+        rnd = lambda *shape: torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+        sets = [(rnd(w.B, w.Hkv, lcap, w.D), rnd(w.B, w.Hkv, lcap, w.D)) for _ in range(3)]
+        q, kb, vb = rnd(w.B, w.S, w.Hq, w.D), rnd(w.B, w.S, w.Hkv, w.D), rnd(w.B, w.S, w.Hkv, w.D)
+        lens = torch.from_numpy(lens_np).to(dev)
+        ad = bd.attn_desc(w.B, w.Hq, w.Hkv, w.D, w.S, lcap, lcap)
+        ws = torch.empty(max(bd.attn_workspace_bytes(ad), 1), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        tr = bd.Trace(capacity=64)
+        with tr:
+            for i in range(7):
+                kc, vc = sets[i % 3]
+                bd.attn_step(q, kb, vb, kc, vc, lens, out=out, want_lse=False, max_prefix_len=lcap, workspace=ws)
+        per = {}
+        for n, ms in tr.records():
+            per.setdefault(n, []).append(ms)
+        tr.clear()
+        split = float(np.mean(per["attn_split"][1:])) * 1e3
+        merge = float(np.mean(per["attn_merge"][1:])) * 1e3 if per.get("attn_merge") else 0.0
+        fl, kv, qb = attn_units(w, lens_np, np.ones(w.B, bool))
+        at = split + merge
+        del sets
+        torch.cuda.synchronize()
+        logit_sets = [(torch.randn((w.B * w.S, w.V), generator=g, device=dev) * 3.0).to(torch.bfloat16)
+                      for _ in range(3)]
+        mask_np = I.initial_mask(w)
+        mask0 = torch.from_numpy(mask_np).to(dev)
+        mask = mask0.clone()
+        tok = torch.zeros(w.B * w.S, dtype=torch.int32, device=dev)
+        ud = bd.unmask_desc(w.B, w.S, w.V, None, True, w.gamma, True, False)
+        uws = torch.empty(max(bd.unmask_workspace_bytes(ud), 1), dtype=torch.uint8, device=dev)
+        with tr:
+            for i in range(7):
+                mask.copy_(mask0)
+                bd.confidence_unmask(logit_sets[i % 3], mask, tok, w.S, w.gamma, outputs=False, workspace=uws)
+        per = {}
+        for n, ms in tr.records():
+            per.setdefault(n, []).append(ms)
+        tr.close()
+        red = float(np.mean(per["vocab_reduce"][1:])) * 1e3
+        com = float(np.mean(per["commit"][1:])) * 1e3
+        nm = int(mask_np.sum())
+        pos_s = nm / ((red + com) * 1e-6)
+        roof = HBM_PEAK_GBS * 1e9 / (w.V * 2)
+        out_rows[name] = {
+            "workload": f"{name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} S={w.S} L={w.prefix_len} V={w.V}",
+            "attn": {"split_us": round(split, 2), "merge_us": round(merge, 2),
+                     "tflops": round(fl / (at * 1e-6) / 1e12, 1),
+                     "mfma_frac": round(fl / (at * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "gbs": round((kv + qb) / (at * 1e-6) / 1e9, 1),
+                     "frac_hbm": round((kv + qb) / (at * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "frac_hbm_split_only": round((kv + qb) / (split * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes": int(kv + qb), "flops": int(fl)},
+            "unmask": {"masked_rows": nm, "reduce_us": round(red, 2), "commit_us": round(com, 2),
+                       "positions_per_s": round(pos_s, 1), "frac_roofline": round(pos_s / roof, 4),
+                       "reduce_gbs": round(nm * w.V * 2 / (red * 1e-6) / 1e9, 1)},
+        }
+        del logit_sets, q, kb, vb, ws, out
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out_rows
 
 
 def measured_traffic(kernel_source: str):
@@ -270,6 +314,7 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--sets", type=int, default=3, help="independent prefix caches rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-config-rows", action="store_true", help="skip the per-workload attention/unmask rows")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (5 times): the reference for HBM byte counters")
@@ -441,6 +486,12 @@ def main():
     }
     line["rows"] = row_figures(args, w, bd, torch, dev, recs, steps_used, commits, mask0, lens, ad, ws, dq, dlog,
                                caches, lens_d, is_bf16, T)
+    # the same kernel over the launches of full steps only (every sequence active)
+    line["roofline"]["frac_full_step_launches"] = line["rows"]["attn_split"]["frac_hbm"]
+    if not args.no_config_rows:
+        del caches, dq, dlog
+        torch.cuda.empty_cache()
+        line["configs"] = config_rows(bd, dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, inp0, logits_np[0], mask0, args.cpu_budget)

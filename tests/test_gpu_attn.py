@@ -198,12 +198,13 @@ def test_tile_edges_of_the_long_prefix_kernel(lens, D, num_splits, causal):
 
 
 MANY = [
-    # name, Hq, Hkv, D, num_splits: 512 sequences; 64 rows per KV head plans the four-wave kernel,
-    # 256 rows the eight-wave one; forced splits run the merge and the device re-plan over the
-    # active sequences
-    ("many-4w", 8, 2, 64, 0),
-    ("many-8w", 32, 2, 128, 0),
-    ("many-8w-split3", 32, 2, 128, 3),
+    # name, Hq, Hkv, D, num_splits, waves: 512 sequences; 64 and 128 rows per KV head plan the
+    # four-wave kernel (with 64 rows half its waves hold no rows), 256 rows the eight-wave one;
+    # forced splits run the merge and the device re-plan over the active sequences
+    ("many-4w-64rows", 8, 2, 64, 0, 4),
+    ("many-4w", 16, 2, 64, 2, 4),
+    ("many-8w", 32, 2, 128, 0, 8),
+    ("many-8w-split3", 32, 2, 128, 3, 8),
 ]
 
 
@@ -212,7 +213,7 @@ def test_many_sequences_with_a_ragged_active_mask(case):
     """512 sequences, a seeded ragged active mask (first inactive, last active): the work-groups
     find their sequence and the merge its partial rows through the work-group scan of the flags.
     Active rows match the oracle; inactive rows keep the canary fill."""
-    name, Hq, Hkv, D, num_splits = case
+    name, Hq, Hkv, D, num_splits, waves = case
     B = 512
     w = I.small_workload(name, B=B, Hq=Hq, Hkv=Hkv, D=D, S=16, prefix_len=(60, 700), wid=340 + MANY.index(case))
     inp = I.attn_inputs(w)
@@ -220,7 +221,7 @@ def test_many_sequences_with_a_ragged_active_mask(case):
     act[0], act[-1] = 0, 1
     plan = bd.attn_plan(bd.attn_desc(B, Hq, Hkv, D, 16, inp["k_cache"].shape[2], int(inp["prefix_len"].max()),
                                      num_splits=num_splits))
-    assert plan["waves"] == (8 if Hq == 32 else 4), plan
+    assert plan["waves"] == waves, plan
     print(f"[attn] {name} active={int(act.sum())} plan={plan}", flush=True)
     t = {k: dev_bf16(inp[k]) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
     big, out, gd = guarded(tuple(inp["q"].shape), torch.bfloat16)
