@@ -40,6 +40,15 @@ bd_status fail(bd_status st, const char* fmt, ...) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// A C caller may store any int in a bd_dtype field; reading an out-of-range value through the C++
+// enum type is undefined, so validation reads the field's bytes as the int the ABI passes.
+static_assert(sizeof(bd_dtype) == sizeof(int32_t), "bd_dtype is passed as a 32-bit int");
+int32_t dtype_value(const bd_dtype& f) {
+  int32_t v;
+  std::memcpy(&v, &f, sizeof(v));
+  return v;
+}
+
 constexpr int kCUs = 256;                  // MI355X compute units
 constexpr size_t kLdsPerCU = 160 * 1024;   // bytes of LDS per compute unit
 constexpr int64_t kMinChunk = 256;         // keys per split below which splitting does not pay
@@ -205,8 +214,9 @@ bd_status check_unmask_desc(const bd_unmask_desc* d) {
   if (d->block_len < 1 || d->block_len > 64) return fail(BD_EINVAL, "block_len must be in [1, 64] (got %d)", d->block_len);
   if (d->vocab < 1) return fail(BD_EINVAL, "vocab must be >= 1");
   if (d->row_stride < d->vocab) return fail(BD_EINVAL, "row_stride must be >= vocab");
-  if (d->logits_dtype != BD_BF16 && d->logits_dtype != BD_F32) return fail(BD_EINVAL, "logits_dtype must be BD_BF16 or BD_F32");
-  const int elt = d->logits_dtype == BD_BF16 ? 2 : 4;
+  const int32_t dt = dtype_value(d->logits_dtype);
+  if (dt != BD_BF16 && dt != BD_F32) return fail(BD_EINVAL, "logits_dtype must be BD_BF16 or BD_F32");
+  const int elt = dt == BD_BF16 ? 2 : 4;
   if ((d->row_stride * elt) % 16 != 0) return fail(BD_EINVAL, "row_stride * element size must be a multiple of 16 bytes");
   if (!(d->gamma >= 0.f && d->gamma <= 1.f)) return fail(BD_EINVAL, "gamma must be in [0, 1]");
   if ((d->min_commit != 0 && d->min_commit != 1) || (d->commit_all != 0 && d->commit_all != 1))
@@ -289,8 +299,9 @@ bd_status check_halt_desc(const bd_halt_desc* d) {
   if (!d) return fail(BD_EINVAL, "halting descriptor is NULL");
   if (d->batch < 1) return fail(BD_EINVAL, "batch must be >= 1");
   if (d->n_per_seq < 1) return fail(BD_EINVAL, "n_per_seq must be >= 1");
-  if (d->dtype != BD_BF16 && d->dtype != BD_F32) return fail(BD_EINVAL, "dtype must be BD_BF16 or BD_F32");
-  const int elt = d->dtype == BD_BF16 ? 2 : 4;
+  const int32_t dt = dtype_value(d->dtype);
+  if (dt != BD_BF16 && dt != BD_F32) return fail(BD_EINVAL, "dtype must be BD_BF16 or BD_F32");
+  const int elt = dt == BD_BF16 ? 2 : 4;
   if ((d->n_per_seq * elt) % 16 != 0) return fail(BD_EINVAL, "n_per_seq * element size must be a multiple of 16 bytes");
   if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return fail(BD_EINVAL, "eps must be finite and >= 0");
   if (d->max_iter < 1) return fail(BD_EINVAL, "max_iter must be >= 1");
