@@ -40,6 +40,11 @@ states. Sources (page title, section):
   the looped mid-block stops when the relative change of the hidden state
   between consecutive loop iterations falls below epsilon, or when the
   iteration budget is reached.
+* Block-local bidirectional Mamba scan (BDLM Mamba-H) -- Hybrid Block Diffusion
+  with Partial Bidirectionality summary, technical §Method: completed prefix
+  blocks keep only the forward scan's boundary (recurrent) state; the reverse
+  scan is confined to the active block, so the cached prefix state is a
+  function of the clean prefix alone.
 
 Readings where the pages are silent:
 one softmax over prefix keys followed by block keys; every prefix key visible
@@ -61,6 +66,12 @@ verification commits at least one token). Loop halting: per sequence, the
 relative change is ||h_cur - h_prev||_2 / ||h_prev||_2 over all its positions and
 hidden units (0/0 counts as no change); the loop halts after iteration k
 (1-based) when that change is below epsilon or k has reached the budget.
+Mamba-H scan (the pages name the Mamba mixer but print no recurrence): the
+Mamba-2 selective scan per head -- a scalar decay exp(dt A) per position, an
+input dt B x^T, an output C^T H -- forward from the cached boundary state over
+the block, reverse from a zero state over the block only, the two outputs
+summed with a skip term D x; the step sizes, decay rates and the B, C, x
+projections are inputs, as q, k, v are for the attention.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 things other than itself (library routines for special cases, closed forms,
@@ -444,3 +455,67 @@ def denoise_block(T: int, t0: int, B: int, S: int, mask0, tokens0, step_inputs: 
         steps_used[active] = t + 1
     return {"mask": mask, "tokens": tokens, "steps_used": steps_used, "commits": commits,
             "outs": outs, "conf": confs, "argmax": argmaxes, "active": actives, "masks": masks}
+
+
+# ----------------------------------------------------------------------------------------------
+# block-local bidirectional Mamba scan (BDLM Mamba-H)
+# ----------------------------------------------------------------------------------------------
+def _group_of(h: int, H: int, G: int) -> int:
+    """Head h reads B and C of group floor(h * G / H) (contiguous groups, as for GQA)."""
+    return (h * G) // H
+
+
+def mamba_block_scan(h0, fwd, rev, A, A_r, D_skip):
+    """One Mamba-H mixer pass over the active block of every sequence, float64.
+
+    h0 [B, H, N, P]: the cached forward boundary state (the forward scan's state after the clean
+    prefix). fwd and rev: the block's per-position inputs of the forward and of the reverse
+    direction, dicts with x [B, S, H, P], dt [B, S, H] (step sizes > 0), Bm and Cm [B, S, G, N].
+    A, A_r [H]: decay rates (< 0); D_skip [H].
+
+    Forward, state F_{-1} = h0:   F_s = exp(dt_s A) F_{s-1} + dt_s Bm_s x_s^T,   yf_s = Cm_s^T F_s
+    Reverse, state R_S = 0:       R_s = exp(dtr_s A_r) R_{s+1} + dtr_s Bmr_s xr_s^T,  yr_s = Cmr_s^T R_s
+    (s = S-1 down to 0: the reverse scan sees the block's positions only)
+    y_s = yf_s + yr_s + D_skip x_s.
+    Returns y [B, S, H, P] and h_out [B, H, N, P] = F_{S-1}, the forward state after the block
+    (the cache entry once the block is committed)."""
+    B, S, H, P = fwd["x"].shape
+    G = fwd["Bm"].shape[2]
+    y = np.zeros((B, S, H, P))
+    h_out = np.zeros(np.shape(h0))
+    for b in range(B):
+        for h in range(H):
+            g = _group_of(h, H, G)
+            F = np.array(h0[b, h], dtype=np.float64)
+            for s in range(S):
+                F = np.exp(fwd["dt"][b, s, h] * A[h]) * F + fwd["dt"][b, s, h] * np.outer(fwd["Bm"][b, s, g],
+                                                                                          fwd["x"][b, s, h])
+                y[b, s, h] += fwd["Cm"][b, s, g] @ F
+            h_out[b, h] = F
+            R = np.zeros_like(F)
+            for s in range(S - 1, -1, -1):
+                R = np.exp(rev["dt"][b, s, h] * A_r[h]) * R + rev["dt"][b, s, h] * np.outer(rev["Bm"][b, s, g],
+                                                                                             rev["x"][b, s, h])
+                y[b, s, h] += rev["Cm"][b, s, g] @ R
+            y[b, :, h] += D_skip[h] * fwd["x"][b, :, h]
+    return y, h_out
+
+
+def mamba_sequence(fwd, rev, A, A_r, D_skip, S: int, h_init=None):
+    """A whole sequence of blocks of S positions the way BDLM Mamba-H runs it: one forward scan
+    over every position from h_init (zero by default), and a reverse scan restarted from zero in
+    every block. fwd / rev hold x [B, L, H, P], dt [B, L, H], Bm / Cm [B, L, G, N] with L a
+    multiple of S. Returns (y [B, L, H, P], the forward boundary states after every block
+    [B, L/S, H, N, P])."""
+    B, L, H, P = fwd["x"].shape
+    N = fwd["Bm"].shape[3]
+    state = np.zeros((B, H, N, P)) if h_init is None else np.array(h_init, dtype=np.float64)
+    ys, bounds = [], []
+    for k in range(L // S):
+        sl = slice(k * S, (k + 1) * S)
+        blk_f = {n: v[:, sl] for n, v in fwd.items()}
+        blk_r = {n: v[:, sl] for n, v in rev.items()}
+        y, state = mamba_block_scan(state, blk_f, blk_r, A, A_r, D_skip)
+        ys.append(y)
+        bounds.append(state)
+    return np.concatenate(ys, axis=1), np.stack(bounds, axis=1)
