@@ -289,6 +289,48 @@ def config_rows(bd, dev):
     return out_rows
 
 
+def mamba_row(bd, dev):
+    """The block-local bidirectional Mamba scan at its measured shape (32 sequences x 64 heads x
+    P 64, N 128 in 8 groups, S 16): a denoising step (y only: the cached boundary state is read,
+    not advanced) and the committing pass (y and the new boundary state). Inputs seeded on the
+    device (x, B, C ~ N(0,1) bf16 with B, C scaled by N^-1/2; dt ~ U[0.01, 0.2]; A ~ -U[1, 16]);
+    three state sets rotate so that no launch finds h0 in the Infinity Cache. Algorithmic bytes:
+    h0 read (+ h_out written), x and dt of both directions, B and C of both directions, y written,
+    A, A_r and D."""
+    import torch
+    B, S, H, G, N, P = 32, 16, 64, 8, 128, 64
+    g = torch.Generator(device=dev)
+    g.manual_seed(20261206)
+    bf = lambda *shape, sc=1.0: (torch.randn(shape, generator=g, device=dev) * sc).to(torch.bfloat16)
+    uni = lambda *shape, lo, hi: torch.rand(shape, generator=g, device=dev) * (hi - lo) + lo
+    sides = [(bf(B, S, H, P), uni(B, S, H, lo=0.01, hi=0.2), bf(B, S, G, N, sc=N ** -0.5), bf(B, S, G, N, sc=N ** -0.5))
+             for _ in range(2)]
+    A, Ar = -uni(H, lo=1.0, hi=16.0), -uni(H, lo=1.0, hi=16.0)
+    D = torch.randn(H, generator=g, device=dev)
+    states = [torch.randn((B, H, N, P), generator=g, device=dev) for _ in range(3)]
+    y = torch.empty((B, S, H, P), dtype=torch.bfloat16, device=dev)
+    h_out = torch.empty_like(states[0])
+    inputs = 2 * (B * S * H * P * 2 + B * S * H * 4 + 2 * B * S * G * N * 2) + B * S * H * P * 2 + 3 * H * 4
+    state = B * H * N * P * 4
+    res = {"workload": f"mamba_h: B={B} H={H} P={P} N={N} G={G} S={S}"}
+    for name, want in (("step", False), ("commit", True)):
+        tr = bd.Trace(capacity=64)
+        with tr:
+            for i in range(7):
+                bd.mamba_block_scan(states[i % 3], sides[0], sides[1], A, Ar, D, y=y, h_out=h_out if want else None,
+                                    want_h_out=want)
+        ms = [m for n, m in tr.records() if n == "mamba_block"]
+        tr.close()
+        us = float(np.mean(ms[1:])) * 1e3
+        nbytes = inputs + state * (2 if want else 1)
+        res[name] = {"us": round(us, 2), "bytes": int(nbytes), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del states, sides, y, h_out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def measured_traffic(kernel_source: str):
     """HBM traffic per launch of the attention split kernel from the committed counter summary
     (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a plain copy kernel), or None when the summary
@@ -492,6 +534,8 @@ def main():
         del caches, dq, dlog
         torch.cuda.empty_cache()
         line["configs"] = config_rows(bd, dev)
+        print("[bench] row mamba_h", file=sys.stderr, flush=True)
+        line["configs"]["mamba_h"] = mamba_row(bd, dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, inp0, logits_np[0], mask0, args.cpu_budget)

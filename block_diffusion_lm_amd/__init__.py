@@ -12,6 +12,7 @@ no CPU or PyTorch fallback: a missing library raises.
     kv_append(k_new, v_new, k_cache, v_cache, prefix_len, ...)  prefix-cache append
     spec_verify(logits, draft, first_choice, block_len, ...)     self-speculation acceptance
     loop_halt(h_prev, h_cur, iteration, eps, max_iter, ...)      adaptive loop halting
+    mamba_block_scan(h0, fwd, rev, A, A_r, D, ...)               block-local bidirectional Mamba scan
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ from ._lib import AttnDesc, BdError, HaltDesc, StepHooks, UnmaskDesc  # noqa: F4
 
 __all__ = ["attn_step", "attn_plan", "confidence_unmask", "confidence_unmask_noalloc", "denoise_block", "attn_desc", "unmask_desc", "Trace", "BdError",
            "attn_workspace_bytes", "unmask_workspace_bytes", "denoise_workspace_bytes", "version", "kv_append",
-           "spec_verify", "loop_halt", "halt_desc", "loop_halt_workspace_bytes"]
+           "spec_verify", "loop_halt", "halt_desc", "loop_halt_workspace_bytes", "mamba_block_scan"]
 
 
 def _torch():
@@ -355,6 +356,45 @@ def denoise_block(get_qkv: Optional[Callable], get_logits: Optional[Callable], k
         raise errors[0]
     _lib.check(st, "bd_denoise_block")
     return {"out": out, "steps_used": steps_used, "commits_per_step": cps}
+
+
+def mamba_block_scan(h0, fwd, rev, A, A_r, D, active=None, y=None, h_out=None, want_h_out=True, stream=None):
+    """bd_mamba_block_scan on torch tensors. h0 [B,H,N,P] float32 (the cached forward boundary
+    state); fwd / rev: (x [B,S,H,P] bf16, dt [B,S,H] float32, Bm [B,S,G,N] bf16, Cm [B,S,G,N] bf16)
+    of the forward and the reverse direction; A, A_r, D [H] float32. Returns (y [B,S,H,P] bf16,
+    h_out [B,H,N,P] float32 or None)."""
+    torch = _torch()
+    L = _lib.load()
+    _dev_tensor(h0, "h0", torch.float32)
+    B, H, N, P = h0.shape
+    dirs = []
+    for name, (x, dt, Bm, Cm), Ad in (("fwd", fwd, A), ("rev", rev, A_r)):
+        _dev_tensor(x, f"{name} x", torch.bfloat16)
+        _dev_tensor(dt, f"{name} dt", torch.float32)
+        _dev_tensor(Bm, f"{name} Bm", torch.bfloat16)
+        _dev_tensor(Cm, f"{name} Cm", torch.bfloat16)
+        _dev_tensor(Ad, f"{name} A", torch.float32)
+        S = x.shape[1]
+        G = Bm.shape[2]
+        if x.shape != (B, S, H, P) or dt.shape != (B, S, H) or Bm.shape != (B, S, G, N) or Cm.shape != Bm.shape \
+                or Ad.shape != (H,):
+            raise ValueError(f"{name} inputs must be x [B,S,H,P], dt [B,S,H], Bm/Cm [B,S,G,N], A [H]")
+        dirs.append(_lib.MambaDir(_ptr(x), _ptr(dt), _ptr(Bm), _ptr(Cm), _ptr(Ad)))
+    if fwd[0].shape != rev[0].shape or fwd[2].shape != rev[2].shape:
+        raise ValueError("forward and reverse inputs must have the same shapes")
+    _dev_tensor(D, "D", torch.float32)
+    if active is not None:
+        _dev_tensor(active, "active", torch.uint8)
+    S, G = fwd[0].shape[1], fwd[2].shape[2]
+    desc = _lib.MambaDesc(B, H, G, P, N, S)
+    if y is None:
+        y = torch.empty((B, S, H, P), dtype=torch.bfloat16, device=h0.device)
+    if h_out is None and want_h_out:
+        h_out = torch.empty_like(h0)
+    _lib.check(L.bd_mamba_block_scan(ctypes.byref(desc), _ptr(h0), ctypes.byref(dirs[0]), ctypes.byref(dirs[1]),
+                                     _ptr(D), _ptr(active), _ptr(y), _ptr(h_out), _stream(stream)),
+               "bd_mamba_block_scan")
+    return y, h_out
 
 
 class Trace:

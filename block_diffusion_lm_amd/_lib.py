@@ -51,6 +51,22 @@ class UnmaskDesc(ctypes.Structure):
     ]
 
 
+class MambaDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("n_groups", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("state_dim", ctypes.c_int32),
+        ("block_len", ctypes.c_int32),
+    ]
+
+
+class MambaDir(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("dt", ctypes.c_void_p), ("Bm", ctypes.c_void_p), ("Cm", ctypes.c_void_p),
+                ("A", ctypes.c_void_p)]
+
+
 class HaltDesc(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32),
@@ -83,7 +99,7 @@ EXPORTS = [
     "bd_denoise_workspace_bytes", "bd_denoise_block", "bd_last_error", "bd_trace_create", "bd_trace_destroy",
     "bd_trace_attach", "bd_trace_clear", "bd_trace_count", "bd_trace_get", "bd_version", "bd_table_hooks",
     "bd_kv_append", "bd_spec_verify", "bd_loop_halt_workspace_bytes", "bd_loop_halt",
-    "bd_confidence_unmask_noalloc", "bd_attn_plan",
+    "bd_confidence_unmask_noalloc", "bd_attn_plan", "bd_mamba_block_scan",
 ]
 
 _lib = None
@@ -129,6 +145,8 @@ def load() -> ctypes.CDLL:
     L.bd_unmask_workspace_bytes.restype = sz
     L.bd_confidence_unmask.argtypes = [P(UnmaskDesc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.bd_confidence_unmask.restype = ctypes.c_int
+    L.bd_mamba_block_scan.argtypes = [P(MambaDesc), vp, P(MambaDir), P(MambaDir), vp, vp, vp, vp, vp]
+    L.bd_mamba_block_scan.restype = ctypes.c_int
     L.bd_attn_plan.argtypes = [P(AttnDesc), P(AttnPlanInfo)]
     L.bd_attn_plan.restype = ctypes.c_int
     L.bd_confidence_unmask_noalloc.argtypes = [P(UnmaskDesc), vp, vp, vp, vp, vp, vp, vp]

@@ -520,6 +520,58 @@ bd_status bd_loop_halt(const bd_halt_desc* desc, const void* h_prev, const void*
   return traced("halt_final", s, [&](const bd::Launch& l) { return bd::launch_halt_final(a, l); });
 }
 
+bd_status bd_mamba_block_scan(const bd_mamba_desc* desc, const float* h0, const bd_mamba_dir* fwd,
+                              const bd_mamba_dir* rev, const float* D, const uint8_t* active, void* y, float* h_out,
+                              void* stream) {
+  if (!desc) return fail(BD_EINVAL, "Mamba descriptor is NULL");
+  if (desc->batch < 1 || desc->n_heads < 1 || desc->n_groups < 1) return fail(BD_EINVAL, "batch, heads and groups must be >= 1");
+  if (desc->n_heads % desc->n_groups != 0)
+    return fail(BD_EINVAL, "n_heads (%d) must be a multiple of n_groups (%d)", desc->n_heads, desc->n_groups);
+  if (desc->head_dim != 64) return fail(BD_EUNSUPPORTED, "head_dim %d is not supported (64)", desc->head_dim);
+  if (desc->state_dim != 64 && desc->state_dim != 128)
+    return fail(BD_EUNSUPPORTED, "state_dim %d is not supported (64 or 128)", desc->state_dim);
+  if (desc->block_len < 1 || desc->block_len > 32) return fail(BD_EINVAL, "block_len must be in [1, 32] (got %d)", desc->block_len);
+  if ((int64_t)desc->batch * desc->n_heads > 0x7fffffff) return fail(BD_EUNSUPPORTED, "batch * n_heads too large");
+  if (!fwd || !rev) return fail(BD_EINVAL, "direction inputs are NULL");
+  const bd_mamba_dir* dirs[2] = {fwd, rev};
+  for (int d = 0; d < 2; ++d) {
+    const bd_mamba_dir* r = dirs[d];
+    const void* req[] = {r->x, r->dt, r->Bm, r->Cm, r->A};
+    const char* names[] = {"x", "dt", "Bm", "Cm", "A"};
+    for (int i = 0; i < 5; ++i)
+      if (!req[i] || !aligned(req[i], 16))
+        return fail(BD_EINVAL, "%s %s is NULL or not 16-byte aligned", d ? "reverse" : "forward", names[i]);
+  }
+  const void* req[] = {h0, D, y};
+  const char* names[] = {"h0", "D", "y"};
+  for (int i = 0; i < 3; ++i)
+    if (!req[i] || !aligned(req[i], 16)) return fail(BD_EINVAL, "%s is NULL or not 16-byte aligned", names[i]);
+  if (h_out && !aligned(h_out, 16)) return fail(BD_EINVAL, "h_out is not 16-byte aligned");
+  bd::MambaArgs a{};
+  a.h0 = h0;
+  a.x = static_cast<const uint16_t*>(fwd->x);
+  a.dt = fwd->dt;
+  a.Bm = static_cast<const uint16_t*>(fwd->Bm);
+  a.Cm = static_cast<const uint16_t*>(fwd->Cm);
+  a.A = fwd->A;
+  a.x_r = static_cast<const uint16_t*>(rev->x);
+  a.dt_r = rev->dt;
+  a.Bm_r = static_cast<const uint16_t*>(rev->Bm);
+  a.Cm_r = static_cast<const uint16_t*>(rev->Cm);
+  a.A_r = rev->A;
+  a.D = D;
+  a.active = active;
+  a.y = static_cast<uint16_t*>(y);
+  a.h_out = h_out;
+  a.B = desc->batch;
+  a.S = desc->block_len;
+  a.H = desc->n_heads;
+  a.G = desc->n_groups;
+  a.N = desc->state_dim;
+  return traced("mamba_block", static_cast<hipStream_t>(stream),
+                [&](const bd::Launch& l) { return bd::launch_mamba_block(a, l); });
+}
+
 size_t bd_denoise_workspace_bytes(const bd_attn_desc* attn, const bd_unmask_desc* unmask) {
   if (check_attn_desc(attn) != BD_OK || check_unmask_desc(unmask) != BD_OK) return 0;
   if (attn->batch != unmask->batch || attn->block_len != unmask->block_len) return 0;

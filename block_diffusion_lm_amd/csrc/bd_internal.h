@@ -1,5 +1,5 @@
 // Internal interface between the host side of the library (bd_api.cpp) and the HIP kernels
-// (bd_attn.hip, bd_unmask.hip, bd_cache.hip, bd_halt.hip). Not installed; the public ABI is
+// (bd_attn.hip, bd_unmask.hip, bd_cache.hip, bd_halt.hip, bd_mamba.hip). Not installed; the public ABI is
 // include/bd.h.
 #pragma once
 
@@ -163,6 +163,30 @@ struct HaltArgs {
 };
 
 hipError_t launch_halt_reduce(const HaltArgs& a, const Launch& l);
+
+// ---------------------------------------------------------------------------------------------
+// block-local bidirectional Mamba scan
+// ---------------------------------------------------------------------------------------------
+struct MambaArgs {
+  const float* h0;          // [B, H, N, P] cached forward boundary state
+  const uint16_t* x;        // [B, S, H, P] bf16, forward direction
+  const float* dt;          // [B, S, H]
+  const uint16_t* Bm;       // [B, S, G, N] bf16
+  const uint16_t* Cm;
+  const float* A;           // [H]
+  const uint16_t* x_r;      // reverse direction, same shapes
+  const float* dt_r;
+  const uint16_t* Bm_r;
+  const uint16_t* Cm_r;
+  const float* A_r;
+  const float* D;           // [H] skip
+  const uint8_t* active;    // [B] or nullptr
+  uint16_t* y;              // [B, S, H, P] bf16
+  float* h_out;             // [B, H, N, P] or nullptr
+  int B, S, H, G, N;        // head_dim P = 64
+};
+
+hipError_t launch_mamba_block(const MambaArgs& a, const Launch& l);
 hipError_t launch_halt_final(const HaltArgs& a, const Launch& l);
 hipError_t launch_len_advance(const AppendArgs& a, const Launch& l);
 

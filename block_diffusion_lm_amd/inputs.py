@@ -36,6 +36,7 @@ TENSOR_IDS = {
     "q": 0, "k_blk": 1, "v_blk": 2, "k_cache": 3, "v_cache": 4,
     "logits": 5, "mask": 6, "peaks": 7, "lens": 8, "ties": 9,
     "h_prev": 10, "h_delta": 11,
+    "m_h0": 12, "m_x": 13, "m_dt": 14, "m_B": 15, "m_C": 16, "m_A": 17, "m_D": 18,
 }
 
 
@@ -268,3 +269,22 @@ def loop_states(wid: int, B: int, n: int, scales, bf16: bool = True, zero_prev=(
     if bf16:
         return f32_to_bf16_bits(x).reshape(B, n), f32_to_bf16_bits(y).reshape(B, n)
     return x, y
+
+
+def mamba_inputs(wid: int, B: int, S: int, H: int, G: int, N: int, P: int = 64) -> dict:
+    """Inputs of one block-local bidirectional Mamba scan: the cached boundary state h0 ~ N(0,1)
+    float32 [B,H,N,P]; per direction (forward = step 0, reverse = step 1 of the seeds) x ~ N(0,1)
+    bf16 [B,S,H,P], B and C ~ N(0,1)/sqrt(N) bf16 [B,S,G,N], step sizes dt ~ U[0.01, 0.2] float32
+    [B,S,H] and decay rates A = -U[1, 16] float32 [H] (the range of Mamba-2's initialisation);
+    skip D ~ N(0,1) float32 [H]. bf16 tensors are uint16 bit patterns."""
+    def side(step):
+        x = normal_bf16(rng(wid, "m_x", step), (B, S, H, P))
+        sc = np.float32(1.0 / np.sqrt(N))
+        Bm = f32_to_bf16_bits(rng(wid, "m_B", step).standard_normal((B, S, G, N), dtype=np.float32) * sc)
+        Cm = f32_to_bf16_bits(rng(wid, "m_C", step).standard_normal((B, S, G, N), dtype=np.float32) * sc)
+        dt = rng(wid, "m_dt", step).uniform(0.01, 0.2, size=(B, S, H)).astype(np.float32)
+        A = (-rng(wid, "m_A", step).uniform(1.0, 16.0, size=H)).astype(np.float32)
+        return {"x": x, "dt": dt, "Bm": Bm, "Cm": Cm, "A": A}
+    return {"h0": rng(wid, "m_h0").standard_normal((B, H, N, P), dtype=np.float32),
+            "fwd": side(0), "rev": side(1),
+            "D": rng(wid, "m_D").standard_normal(H, dtype=np.float32)}

@@ -31,6 +31,9 @@
  *  - Technical summary: LoopMDM, §Adaptive inference: the looped mid-block
  *    stops once the relative hidden-state change between iterations falls
  *    below epsilon or the iteration budget is spent (bd_loop_halt).
+ *  - Hybrid Block Diffusion with Partial Bidirectionality summary, technical
+ *    §Method: the reverse Mamba scan stays inside the active block and the
+ *    forward scan's boundary state is the prefix cache (bd_mamba_block_scan).
  *
  * Conventions (every entry point):
  *  - Pointers are DEVICE pointers unless marked (host). The caller owns every
@@ -251,6 +254,50 @@ size_t bd_loop_halt_workspace_bytes(const bd_halt_desc* desc);
  * iteration: k >= 1; rel: float32 [B] or NULL; halt: uint8 [B] (written). */
 bd_status bd_loop_halt(const bd_halt_desc* desc, const void* h_prev, const void* h_cur, int32_t iteration,
                        float* rel, uint8_t* halt, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Block-local bidirectional Mamba scan (BDLM Mamba-H)
+ *
+ * Hybrid Block Diffusion with Partial Bidirectionality summary, technical §Method: completed
+ * prefix blocks keep only the forward scan's boundary (recurrent) state, and the reverse scan is
+ * confined to the active block, so the cached prefix state is a function of the clean prefix
+ * alone. The pages print no recurrence; this is the Mamba-2 selective scan. For sequence b, head
+ * h (B and C of group g = floor(h G / H)) and block position s (0 .. S-1):
+ *   forward, F_{-1} = h0[b,h]:  F_s = exp(dt_s A_h) F_{s-1} + dt_s B_s x_s^T   (N x P state)
+ *   reverse, R_S = 0:           R_s = exp(dtr_s Ar_h) R_{s+1} + dtr_s Br_s xr_s^T (s = S-1 .. 0)
+ *   y[b,s,h,:] = C_s^T F_s + Cr_s^T R_s + D_h x_s,     h_out[b,h] = F_{S-1}
+ * (B_s, C_s, x_s, dt_s of the forward inputs; Br, Cr, xr, dtr of the reverse inputs). h_out is the
+ * boundary state the block leaves, the cache entry once the block is committed. Computed in
+ * float32 (float32 MFMA) from the closed form of the two recurrences.
+ * ---------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;        /* B >= 1 */
+  int32_t n_heads;      /* H >= 1, H % G == 0 */
+  int32_t n_groups;     /* G >= 1 */
+  int32_t head_dim;     /* P: 64 */
+  int32_t state_dim;    /* N: 64 or 128 */
+  int32_t block_len;    /* S: 1 .. 32 */
+} bd_mamba_desc;
+
+typedef struct {        /* one direction's inputs for the block (device pointers, read only) */
+  const void* x;        /* bf16 [B, S, H, P] */
+  const float* dt;      /* float32 [B, S, H], step sizes (> 0) */
+  const void* Bm;       /* bf16 [B, S, G, N] */
+  const void* Cm;       /* bf16 [B, S, G, N] */
+  const float* A;       /* float32 [H], decay rates (< 0) */
+} bd_mamba_dir;
+
+/* h0: float32 [B, H, N, P]; fwd, rev: host structs of device pointers; D: float32 [H]; active:
+ * uint8 [B] or NULL (inactive sequences are skipped: their y and h_out untouched); y: bf16
+ * [B, S, H, P] (written); h_out: float32 [B, H, N, P] or NULL (written). h_out may be h0 itself
+ * (the cache entry advanced in place: every state element is read before it is written, by the
+ * thread that writes it); otherwise h0 is not written and the buffers must not overlap. Every
+ * pointer 16-byte aligned. No workspace, no allocation. BD_EINVAL: NULL descriptor or pointer,
+ * misalignment, a count < 1, H not a multiple of G, S outside 1 .. 32; BD_EUNSUPPORTED: P != 64,
+ * N not 64 or 128, B * H above 2^31 - 1; launch errors as BD_EHIP. */
+bd_status bd_mamba_block_scan(const bd_mamba_desc* desc, const float* h0, const bd_mamba_dir* fwd,
+                              const bd_mamba_dir* rev, const float* D, const uint8_t* active,
+                              void* y, float* h_out, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * The T-step block loop (Algorithm 1's inner loop)

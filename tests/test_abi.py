@@ -164,6 +164,43 @@ def test_unmask_noalloc_host_checks(L):
     assert L.bd_unmask_workspace_bytes(ctypes.byref(edge)) > 4 << 20
 
 
+def good_mamba():
+    return _lib.MambaDesc(2, 8, 2, 64, 128, 16)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, _lib.BD_EINVAL), ("n_heads", 0, _lib.BD_EINVAL), ("n_groups", 0, _lib.BD_EINVAL),
+    ("n_groups", 3, _lib.BD_EINVAL), ("head_dim", 128, _lib.BD_EUNSUPPORTED), ("state_dim", 96, _lib.BD_EUNSUPPORTED),
+    ("state_dim", 256, _lib.BD_EUNSUPPORTED), ("block_len", 0, _lib.BD_EINVAL), ("block_len", 33, _lib.BD_EINVAL),
+    ("batch", 1 << 28, _lib.BD_EUNSUPPORTED)])
+def test_mamba_descriptor_validation(L, field, value, status):
+    d = good_mamba()
+    setattr(d, field, value)
+    p = ctypes.c_void_p(4096)
+    fw = _lib.MambaDir(p, p, p, p, p)
+    assert L.bd_mamba_block_scan(ctypes.byref(d), p, ctypes.byref(fw), ctypes.byref(fw), p, None, p, p, None) == status
+    assert L.bd_last_error()
+
+
+def test_mamba_pointer_validation(L):
+    d = good_mamba()
+    p, odd = ctypes.c_void_p(4096), ctypes.c_void_p(4100)
+    fw = _lib.MambaDir(p, p, p, p, p)
+
+    def run(h0=p, f=fw, r=fw, D=p, y=p, h_out=p):
+        return L.bd_mamba_block_scan(ctypes.byref(d), h0, ctypes.byref(f) if f else None, ctypes.byref(r) if r else None,
+                                     D, None, y, h_out, None)
+
+    for kw in ({"h0": None}, {"D": None}, {"y": None}, {"f": None}, {"r": None}, {"h0": odd}, {"y": odd}, {"h_out": odd}):
+        assert run(**kw) == _lib.BD_EINVAL, kw
+    for i in range(5):
+        for bad in (None, odd):
+            vals = [p] * 5
+            vals[i] = bad
+            assert run(r=_lib.MambaDir(*vals)) == _lib.BD_EINVAL
+            assert b"reverse" in L.bd_last_error()
+
+
 def test_denoise_validation(L):
     ad = good_attn()
     ud = good_unmask()

@@ -10,7 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "block_diffusion_lm_amd", "csrc")
-SOURCES = ["bd_api.cpp", "bd_attn.hip", "bd_unmask.hip", "bd_cache.hip", "bd_halt.hip"]
+SOURCES = ["bd_api.cpp", "bd_attn.hip", "bd_unmask.hip", "bd_cache.hip", "bd_halt.hip", "bd_mamba.hip"]
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
 
