@@ -101,7 +101,9 @@ bd_status check_attn_desc(const bd_attn_desc* d) {
   return BD_OK;
 }
 
-void plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
+// Plans the attention launches for a validated descriptor. Fails when they would not fit their
+// grids (HIP: at most 2^32 - 1 work-items in x) or the merge's 32-bit row indices.
+bd_status plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
   const int group = d->n_q_heads / d->n_kv_heads;
   p->head_dim = d->head_dim;
   p->rows = d->block_len * group;
@@ -143,13 +145,18 @@ void plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
   p->direct = p->nsplit == 1;
   p->wide_merge = p->nsplit > 16;
   if (p->direct) {
-    p->part_acc_off = p->part_ml_off = p->bytes = 0;
+    p->part_o_off = p->part_ml_off = p->bytes = 0;
   } else {
     const size_t prow = (size_t)p->n_items * tile_rows;
-    p->part_acc_off = 0;
-    p->part_ml_off = align_up(prow * d->head_dim * sizeof(float), 256);
+    p->part_o_off = 0;
+    p->part_ml_off = align_up(prow * d->head_dim * sizeof(uint16_t), 256);
     p->bytes = align_up(p->part_ml_off + prow * 2 * sizeof(float), 256);
   }
+  const int64_t merge_rows = (int64_t)d->batch * d->n_kv_heads * p->rows;
+  if (merge_rows > 0x7fffffff || p->n_items * p->waves * 64 > (int64_t)0xffffffff)
+    return fail(BD_EUNSUPPORTED, "problem too large for one launch: %lld query rows, %lld workgroups",
+                (long long)merge_rows, (long long)p->n_items);
+  return BD_OK;
 }
 
 bd_status check_attn_ptrs(const bd_attn_desc* d, const void* q, const void* kb, const void* vb, const void* kc,
@@ -182,7 +189,7 @@ bd_status run_attn(const bd_attn_desc* d, const bd::AttnPlan& plan, const void* 
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   char* w = static_cast<char*>(ws);
-  a.part_acc = plan.direct ? nullptr : reinterpret_cast<float*>(w + plan.part_acc_off);
+  a.part_o = plan.direct ? nullptr : reinterpret_cast<uint16_t*>(w + plan.part_o_off);
   a.part_ml = plan.direct ? nullptr : reinterpret_cast<float*>(w + plan.part_ml_off);
   a.B = d->batch;
   a.S = d->block_len;
@@ -332,7 +339,7 @@ const char* bd_version(void) { return "bd 0.1.0 gfx950"; }
 size_t bd_attn_workspace_bytes(const bd_attn_desc* desc) {
   if (check_attn_desc(desc) != BD_OK) return 0;
   bd::AttnPlan p;
-  plan_attn(desc, &p);
+  if (plan_attn(desc, &p) != BD_OK) return 0;
   return p.bytes;
 }
 
@@ -341,7 +348,8 @@ bd_status bd_attn_plan(const bd_attn_desc* desc, bd_attn_plan_info* info) {
   if (st != BD_OK) return st;
   if (!info) return fail(BD_EINVAL, "info is NULL");
   bd::AttnPlan p;
-  plan_attn(desc, &p);
+  st = plan_attn(desc, &p);
+  if (st != BD_OK) return st;
   info->waves = p.waves;
   info->rows_per_wave = p.rows_per_wave;
   info->row_tiles = p.row_tiles;
@@ -359,7 +367,8 @@ bd_status bd_attn_step(const bd_attn_desc* desc, const void* q, const void* k_bl
   st = check_attn_ptrs(desc, q, k_blk, v_blk, k_cache, v_cache, prefix_len, out, lse);
   if (st != BD_OK) return st;
   bd::AttnPlan plan;
-  plan_attn(desc, &plan);
+  st = plan_attn(desc, &plan);
+  if (st != BD_OK) return st;
   st = check_ws(workspace, workspace_bytes, plan.bytes);
   if (st != BD_OK) return st;
   return run_attn(desc, plan, q, k_blk, v_blk, k_cache, v_cache, prefix_len, active, out, lse, workspace,
@@ -577,7 +586,7 @@ size_t bd_denoise_workspace_bytes(const bd_attn_desc* attn, const bd_unmask_desc
   if (attn->batch != unmask->batch || attn->block_len != unmask->block_len) return 0;
   bd::AttnPlan ap;
   bd::UnmaskPlan up;
-  plan_attn(attn, &ap);
+  if (plan_attn(attn, &ap) != BD_OK) return 0;
   plan_unmask(unmask, &up);
   return loop_bytes(ap, up, attn->batch);
 }
@@ -603,7 +612,8 @@ bd_status bd_denoise_block(const bd_attn_desc* attn, const bd_unmask_desc* unmas
     return fail(BD_EINVAL, "k_cache / v_cache / prefix_len / out NULL or misaligned");
   bd::AttnPlan ap;
   bd::UnmaskPlan up;
-  plan_attn(attn, &ap);
+  st = plan_attn(attn, &ap);
+  if (st != BD_OK) return st;
   plan_unmask(unmask, &up);
   const size_t need = loop_bytes(ap, up, attn->batch);
   st = check_ws(workspace, workspace_bytes, need);

@@ -160,17 +160,30 @@ struct ActiveScan {
     }
     return found;
   }
-  // the rank of sequence b among the active ones (b's flag need not be set)
-  __device__ int rank(const uint8_t* active, int B, int b) {
-    if (!active) return b;
-    int r = 0;
+  // the number of active sequences and the ranks of sequences b[0..R-1] among them (their flags
+  // need not be set), in one pass over the flags
+  template <int R>
+  __device__ void count_ranks(const uint8_t* active, int B, const int (&b)[R], int& n, int (&r)[R]) {
+    if (!active) {
+      n = B;
+#pragma unroll
+      for (int k = 0; k < R; ++k) r[k] = b[k];
+      return;
+    }
+    n = 0;
+#pragma unroll
+    for (int k = 0; k < R; ++k) r[k] = 0;
     for (int base = 0; base < B; base += NT) {
       load(active, B, base);
-      if (b >= base + NT) r += chunk_count();
-      else if (b >= base) r += rank_in_chunk(b - base);
+      const int c = chunk_count();
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        if (b[k] >= base + NT) r[k] += c;
+        else if (b[k] >= base) r[k] += rank_in_chunk(b[k] - base);
+      }
+      n += c;
       __syncthreads();
     }
-    return r;
   }
 };
 
@@ -781,16 +794,20 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
         }
       if (a.lse && half == 0) a.lse[((int64_t)b * a.Hq + hq) * a.S + s] = (m_run[rb] + log2f(l_tot)) * kLn2;
     } else {
-      // partial (m, l, acc) of this chunk; merged by the merge kernels
+      // partial of this chunk: (m, l) and the normalized output acc / l in bf16 (zero for a chunk
+      // without a visible key); merged by the merge kernel
       const int64_t prow = item_act * tile_rows + (r - rt * tile_rows);
-      float* ap = a.part_acc + prow * D;
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      uint16_t* ap = a.part_o + prow * D;
 #pragma unroll
       for (int db = 0; db < G::DB; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int d = db * 32 + 8 * q4 + 4 * half;
-          const f32x4 v = {o[rb][db][4 * q4], o[rb][db][4 * q4 + 1], o[rb][db][4 * q4 + 2], o[rb][db][4 * q4 + 3]};
-          *reinterpret_cast<f32x4*>(ap + d) = v;
+          bf16x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[rb][db][4 * q4 + i] * inv);
+          *reinterpret_cast<bf16x4*>(ap + d) = v;
         }
       if (half == 0) {
         a.part_ml[prow * 2] = m_run[rb];
@@ -801,19 +818,25 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
   (void)NT;
 }
 
-// Merge of the chunk partials of every (sequence, KV head, query row): with M = max_c m_c,
-//   O = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M),  LSE = (M + log2 sum_c l_c 2^(m_c - M)) ln 2.
+// Merge of the chunk partials of every (sequence, KV head, query row): with M = max_c m_c and the
+// chunk's normalized output o_c = acc_c / l_c (stored in bf16),
+//   O = sum_c l_c 2^(m_c - M) o_c / sum_c l_c 2^(m_c - M),  LSE = (M + log2 sum_c l_c 2^(m_c - M)) ln 2.
+// O is a convex combination of the o_c, so their bf16 rounding (2^-9 relative) bounds its error by
+// 2^-9 max_c |o_c|, the order of the final bf16 rounding of O; the partials cost half the bytes
+// of float32 ones.
 //
-// 256 threads = RW rows x CG chunk groups x (D/4 groups of 4 dims). Chunk group j takes chunks
-// j, j + CG, ... in index order, U at a time (all their loads in flight together), keeping a
-// running maximum: when a group of U raises it, the sums so far are scaled down first. The
-// chunk groups are then combined in index order through LDS, so the result does not depend on
-// scheduling. A chunk without a visible key (m = -inf, causal pass) contributes nothing.
-template <int D, int CG, int U>
+// 256 threads = RW row slots x CG chunk groups x (D/4 groups of 4 dims); a thread of a row slot
+// merges RPT rows (RW x RPT rows per work-group). Chunk group j takes chunks j, j + CG, ... in
+// index order, U at a time for each of its rows (all U x RPT loads in flight together), keeping a
+// running maximum per row: when a group of U raises it, the sums so far are scaled down first.
+// The chunk groups are then combined in index order through LDS, so the result does not depend
+// on scheduling. A chunk without a visible key (m = -inf, causal pass) contributes nothing.
+template <int D, int CG, int U, int RPT>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int tile_rows) {
   constexpr int DG = D / 4;
   constexpr int RW = 256 / (DG * CG);
   static_assert(RW * DG * CG == 256, "thread layout");
+  static_assert(CG == 1 || RPT == 1, "the chunk groups' LDS combine holds one row per thread");
   __shared__ float red_m[CG > 1 ? 256 : 1];
   __shared__ float red_den[CG > 1 ? 256 : 1];
   __shared__ f32x4 red_num[CG > 1 ? 256 : 1];
@@ -821,90 +844,130 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int tile_ro
   const int dg = tid % DG;
   const int cg = (tid / DG) % CG;
   const int rw = tid / (DG * CG);
-  const int64_t rowg = (int64_t)blockIdx.x * RW + rw;
-  const bool live = rowg < (int64_t)a.B * a.Hkv * a.rows;
-  const int r = live ? (int)(rowg % a.rows) : 0;
-  const int pair = live ? (int)(rowg / a.rows) : 0;
-  const int b = pair / a.Hkv;
-  const int g = pair % a.Hkv;
-  const bool act = live && !(a.active && !a.active[b]);
+  // the host keeps B * Hkv * rows below 2^31: 32-bit row arithmetic (no 64-bit division ahead of
+  // the first load)
+  const uint32_t nrows = (uint32_t)a.B * a.Hkv * a.rows;
+  int r[RPT], b[RPT], g[RPT];
+  bool act[RPT];
+  uint32_t plen[RPT];
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const uint32_t rowg = (blockIdx.x * RPT + k) * RW + rw;
+    const bool live = rowg < nrows;
+    const uint32_t pair = live ? rowg / (uint32_t)a.rows : 0;
+    r[k] = live ? (int)(rowg - pair * (uint32_t)a.rows) : 0;
+    b[k] = (int)(pair / (uint32_t)a.Hkv);
+    g[k] = (int)(pair - (uint32_t)b[k] * a.Hkv);
+    // the sequence's length first: it is needed last (to drop the chunks past its keys), and its
+    // load then overlaps the scan of the active flags and the partial loads
+    plen[k] = live ? a.prefix_len[b[k]] : 0;
+    act[k] = live && !(a.active && !a.active[b[k]]);
+  }
   __shared__ uint64_t act_masks[4];
   ActiveScan<256> scan{act_masks};
-  const int n_act = scan.count(a.active, a.B);
+  int n_act, rank_b[RPT];   // every thread takes part in the scan's barriers
+  scan.count_ranks<RPT>(a.active, a.B, b, n_act, rank_b);
   const ItemMap im = device_plan(a, n_act);
   if (im.nsplit == 1) return;   // the split kernel wrote the output itself
-  // ranks of this thread's sequence (every thread takes part in the scan's barriers)
-  const int rank_b = scan.rank(a.active, a.B, b);
-  int ns = 0;
-  int64_t p0 = 0, pstride = 0;
-  if (act) {
-    const int64_t pair_a = (int64_t)rank_b * a.Hkv + g;
-    const int64_t nkeys = (int64_t)a.prefix_len[b] + a.S;
-    ns = (int)min((int64_t)im.nsplit, (nkeys + im.chunk - 1) / im.chunk);
-    const int rt = r / tile_rows;
-    pstride = (int64_t)a.row_tiles * tile_rows;   // partial rows between chunks
-    p0 = ((pair_a * im.nsplit) * a.row_tiles + rt) * tile_rows + (r - rt * tile_rows);
+  const int64_t pstride = (int64_t)a.row_tiles * tile_rows;   // partial rows between chunks
+  int64_t p0[RPT];
+  int ns[RPT];
+  float M[RPT], den[RPT];
+  f32x4 num[RPT];
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    // an inactive row reads the workspace's first rows (in bounds, shared by all such rows) and
+    // drops them: no branch around the loads
+    p0[k] = 0;
+    if (act[k]) {
+      const int64_t pair_a = (int64_t)rank_b[k] * a.Hkv + g[k];
+      const int rt = r[k] / tile_rows;
+      p0[k] = ((pair_a * im.nsplit) * a.row_tiles + rt) * tile_rows + (r[k] - rt * tile_rows);
+    }
+    M[k] = -INFINITY;
+    den[k] = 0.f;
+    num[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float M = -INFINITY, den = 0.f;
-  f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = cg; c0 < ns; c0 += U * CG) {
-    float mm[U], ll[U];
-    f32x4 v[U];
-    // every slot loads (past the last chunk: the last chunk again, then ignored), so that all the
-    // loads of the group are issued before the first is used
+  for (int c0 = cg; c0 < im.nsplit; c0 += U * CG) {
+    float mm[RPT][U], ll[RPT][U];
+    f32x4 v[RPT][U];
+    // every slot loads a chunk of the plan (past the plan's last: the last again), so that all the
+    // loads of the round are issued before the first is used and before the lengths are known;
+    // chunks past a sequence's keys were not written by this call and are dropped here
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int c = min(c0 + j * CG, ns - 1);
-      const int64_t pr = p0 + c * pstride;
-      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
-      mm[j] = c0 + j * CG < ns ? ml.x : -INFINITY;
-      ll[j] = ml.y;
-      v[j] = *reinterpret_cast<const f32x4*>(a.part_acc + pr * D + dg * 4);
-    }
-    float gm = mm[0];
+    for (int k = 0; k < RPT; ++k)
 #pragma unroll
-    for (int j = 1; j < U; ++j) gm = fmaxf(gm, mm[j]);
-    if (gm > M) {
-      const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - gm);
-      den *= sc;
-      num *= sc;
-      M = gm;
-    }
+      for (int j = 0; j < U; ++j) {
+        const int c = min(c0 + j * CG, im.nsplit - 1);
+        const int64_t pr = p0[k] + c * pstride;
+        const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
+        mm[k][j] = ml.x;
+        ll[k][j] = ml.y;
+        const uint2 raw = *reinterpret_cast<const uint2*>(a.part_o + pr * D + dg * 4);
+        v[k][j] = f32x4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                        __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+      }
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const float w = mm[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[j] - M);
-      den += ll[j] * w;
-      num += v[j] * w;
+    for (int k = 0; k < RPT; ++k) {
+      const uint32_t chunk = (uint32_t)im.chunk;   // <= max_prefix_len + S < 2^31
+      ns[k] = act[k] ? (int)min((uint32_t)im.nsplit, (plen[k] + a.S + chunk - 1) / chunk) : 0;
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+        if (c0 + j * CG >= ns[k]) {
+          mm[k][j] = -INFINITY;
+          ll[k][j] = 0.f;
+          v[k][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      float gm = mm[k][0];
+#pragma unroll
+      for (int j = 1; j < U; ++j) gm = fmaxf(gm, mm[k][j]);
+      if (gm > M[k]) {
+        const float sc = M[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[k] - gm);
+        den[k] *= sc;
+        num[k] *= sc;
+        M[k] = gm;
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const float w = mm[k][j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[k][j] - M[k]) * ll[k][j];
+        den[k] += w;
+        num[k] += v[k][j] * w;
+      }
     }
   }
   if constexpr (CG > 1) {
-    red_m[tid] = M;
-    red_den[tid] = den;
-    red_num[tid] = num;
+    red_m[tid] = M[0];
+    red_den[tid] = den[0];
+    red_num[tid] = num[0];
     __syncthreads();
     if (cg != 0) return;
     const int base = rw * DG * CG + dg;
+    float Mc = M[0];
 #pragma unroll
-    for (int j = 1; j < CG; ++j) M = fmaxf(M, red_m[base + j * DG]);
-    den = 0.f;
-    num = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 1; j < CG; ++j) Mc = fmaxf(Mc, red_m[base + j * DG]);
+    den[0] = 0.f;
+    num[0] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
       const float mj = red_m[base + j * DG];
-      const float w = mj == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mj - M);
-      den += red_den[base + j * DG] * w;
-      num += red_num[base + j * DG] * w;
+      const float w = mj == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mj - Mc);
+      den[0] += red_den[base + j * DG] * w;
+      num[0] += red_num[base + j * DG] * w;
     }
+    M[0] = Mc;
   }
-  if (!act) return;
-  const float inv = 1.0f / den;
-  const int s = r / a.group;
-  const int hq = g * a.group + (r - s * a.group);
-  bf16x4 o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = (__bf16)(num[i] * inv);
-  *reinterpret_cast<bf16x4*>(a.out + (((int64_t)b * a.S + s) * a.Hq + hq) * D + dg * 4) = o;
-  if (a.lse && dg == 0) a.lse[((int64_t)b * a.Hq + hq) * a.S + s] = (M + log2f(den)) * kLn2;
+  for (int k = 0; k < RPT; ++k) {
+    if (!act[k]) continue;
+    const float inv = 1.0f / den[k];
+    const int s = r[k] / a.group;
+    const int hq = g[k] * a.group + (r[k] - s * a.group);
+    bf16x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (__bf16)(num[k][i] * inv);
+    *reinterpret_cast<bf16x4*>(a.out + (((int64_t)b[k] * a.S + s) * a.Hq + hq) * D + dg * 4) = o;
+    if (a.lse && dg == 0) a.lse[((int64_t)b[k] * a.Hq + hq) * a.S + s] = (M[k] + log2f(den[k])) * kLn2;
+  }
 }
 
 }  // namespace
@@ -926,19 +989,21 @@ hipError_t launch_attn_split(const AttnPlan& plan, const AttnArgs& a, const Laun
 hipError_t launch_attn_merge(const AttnPlan& plan, const AttnArgs& a, const Launch& l) {
   const int64_t rows = (int64_t)a.B * a.Hkv * a.rows;
   const int tile_rows = plan.waves * plan.rows_per_wave;
-  // many chunks per row: eight chunk groups per row; U: chunks per group and round (2, 4 or 8)
+  // many chunks per row: eight chunk groups per row; U: chunks per group and round (2, 4 or 8);
+  // with one chunk group a thread merges 8 / U rows, so that it keeps eight loads in flight
   const int cg = plan.wide_merge ? 8 : 1;
   const int per = (plan.nsplit + cg - 1) / cg;
   const int u = per <= 2 ? 2 : per <= 4 ? 4 : 8;
+  const int rpt = cg == 1 ? 8 / u : 1;
   const int rw = 256 / ((plan.head_dim / 4) * cg);
-  const dim3 grid((unsigned)((rows + rw - 1) / rw));
+  const dim3 grid((unsigned)((rows + (int64_t)rw * rpt - 1) / ((int64_t)rw * rpt)));
   switch (plan.head_dim * 1000 + cg * 10 + u) {
-#define BD_MERGE(d, c, uu) \
-  case d * 1000 + c * 10 + uu: return launch_kernel(attn_merge_kernel<d, c, uu>, grid, dim3(256), l, a, tile_rows);
-    BD_MERGE(128, 8, 2) BD_MERGE(128, 8, 4) BD_MERGE(128, 8, 8)
-    BD_MERGE(128, 1, 2) BD_MERGE(128, 1, 4) BD_MERGE(128, 1, 8)
-    BD_MERGE(64, 8, 2) BD_MERGE(64, 8, 4) BD_MERGE(64, 8, 8)
-    BD_MERGE(64, 1, 2) BD_MERGE(64, 1, 4) BD_MERGE(64, 1, 8)
+#define BD_MERGE(d, c, uu, rr) \
+  case d * 1000 + c * 10 + uu: return launch_kernel(attn_merge_kernel<d, c, uu, rr>, grid, dim3(256), l, a, tile_rows);
+    BD_MERGE(128, 8, 2, 1) BD_MERGE(128, 8, 4, 1) BD_MERGE(128, 8, 8, 1)
+    BD_MERGE(128, 1, 2, 4) BD_MERGE(128, 1, 4, 2) BD_MERGE(128, 1, 8, 1)
+    BD_MERGE(64, 8, 2, 1) BD_MERGE(64, 8, 4, 1) BD_MERGE(64, 8, 8, 1)
+    BD_MERGE(64, 1, 2, 4) BD_MERGE(64, 1, 4, 2) BD_MERGE(64, 1, 8, 1)
 #undef BD_MERGE
     default: return hipErrorInvalidValue;
   }

@@ -48,7 +48,7 @@ struct AttnPlan {
   int64_t n_items;    // B * Hkv * nsplit * row_tiles workgroups
   bool direct;        // nsplit == 1: the split kernel writes the final output itself
   bool wide_merge;    // many splits: the merge spreads each row's chunks over eight thread groups
-  size_t part_acc_off, part_ml_off, bytes;   // workspace layout
+  size_t part_o_off, part_ml_off, bytes;   // workspace layout
 };
 
 struct AttnArgs {
@@ -61,7 +61,7 @@ struct AttnArgs {
   const uint8_t* active;
   uint16_t* out;
   float* lse;
-  float* part_acc;    // [n_items][rows_pad][D]
+  uint16_t* part_o;   // [n_items][rows_pad][D] bf16: the chunk's normalized output acc / l
   float* part_ml;     // [n_items][rows_pad][2]: running max (log2 units) and sum
   int B, S, Hq, Hkv, group, rows, rows_pad;
   int64_t lcap;

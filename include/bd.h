@@ -104,7 +104,8 @@ typedef struct {
   int32_t causal;           /* 0: bidirectional block (denoiser); 1: causal within the block */
 } bd_attn_desc;
 
-/* Workspace bytes bd_attn_step needs for this descriptor (0 on an invalid descriptor). */
+/* Workspace bytes bd_attn_step needs for this descriptor (0 on an invalid descriptor, or on one
+ * too large for one launch: see bd_attn_step). */
 size_t bd_attn_workspace_bytes(const bd_attn_desc* desc);
 
 /* How bd_attn_step will run a descriptor (host-side query; nothing is enqueued): work-group shape,
@@ -131,7 +132,13 @@ bd_status bd_attn_plan(const bd_attn_desc* desc, bd_attn_plan_info* info);
  *           of out and lse are left untouched.
  * out:      bf16 [B, S, Hq, D]  (written; rounded to nearest even)
  * lse:      float32 [B, Hq, S] or NULL
- * workspace: device scratch of at least bd_attn_workspace_bytes(desc) bytes. */
+ * workspace: device scratch of at least bd_attn_workspace_bytes(desc) bytes.
+ * Errors (all before anything is enqueued): BD_EINVAL for an invalid descriptor, NULL or misaligned
+ * pointer; BD_EWORKSPACE for a workspace below the query; BD_EUNSUPPORTED for an unsupported
+ * head_dim or capacity, and for a problem too large for one launch (B * Hkv * S * Hq / Hkv query
+ * rows at or above 2^31, or a split launch beyond 2^32 - 1 work-items, e.g. with a large forced
+ * num_splits). The output is a convex combination of per-chunk outputs kept in bf16, so it carries
+ * up to twice the rounding of one bf16 result. */
 bd_status bd_attn_step(const bd_attn_desc* desc,
                        const void* q, const void* k_blk, const void* v_blk,
                        const void* k_cache, const void* v_cache,

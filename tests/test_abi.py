@@ -102,6 +102,21 @@ def test_attn_pointer_validation(L):
     assert call_attn(L, d, ws=ctypes.c_void_p(4096 + 16), nbytes=nb) == _lib.BD_EINVAL
 
 
+@pytest.mark.parametrize("desc", [
+    (1 << 16, 1024, 64, 64, 64, 4096, 4096, 0.0, 0),      # 2^32 query rows for the merge
+    (1024, 8, 8, 128, 16, 1 << 20, 1 << 20, 0.0, 1 << 14),  # 2^27 forced-split workgroups of 256 threads
+])
+def test_attn_plan_too_large_for_one_launch(L, desc):
+    """Problems whose launches would not fit a grid (or the merge's 32-bit row indices) are refused
+    before anything is planned into a workspace or enqueued."""
+    d = _lib.AttnDesc(*desc)
+    assert L.bd_attn_workspace_bytes(ctypes.byref(d)) == 0
+    assert call_attn(L, d, nbytes=1 << 40) == _lib.BD_EUNSUPPORTED
+    assert b"too large for one launch" in L.bd_last_error()
+    info = _lib.AttnPlanInfo()
+    assert L.bd_attn_plan(ctypes.byref(d), ctypes.byref(info)) == _lib.BD_EUNSUPPORTED
+
+
 def test_small_problem_needs_no_workspace(L):
     d = _lib.AttnDesc(1, 8, 2, 64, 16, 256, 256, 0.0, 0)
     assert L.bd_attn_workspace_bytes(ctypes.byref(d)) == 0
