@@ -852,7 +852,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int tile_ro
   uint32_t plen[RPT];
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
-    const uint32_t rowg = (blockIdx.x * RPT + k) * RW + rw;
+    // consecutive rows on one XCD: their (m, l) pairs share cache sectors
+    const uint32_t rowg = (xcd_local_item(blockIdx.x, gridDim.x) * RPT + k) * RW + rw;
     const bool live = rowg < nrows;
     const uint32_t pair = live ? rowg / (uint32_t)a.rows : 0;
     r[k] = live ? (int)(rowg - pair * (uint32_t)a.rows) : 0;

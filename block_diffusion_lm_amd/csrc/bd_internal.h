@@ -24,6 +24,17 @@ hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, const Launch& l, Args.
   return hipGetLastError();
 }
 
+// Work item of this work-group such that the work-groups of one XCD take consecutive items. The
+// dispatcher hands work-groups to the eight XCDs in turn (work-group i to XCD i mod 8) and each XCD
+// has its own L2, so items that share data (heads of one B/C group, rows sharing a cache sector)
+// are fetched once per XCD instead of once per work-group. A bijection of [0, n): the first
+// 8 * floor(n / 8) work-groups are regrouped, the rest keep their index.
+constexpr unsigned kXcds = 8;
+__device__ __forceinline__ unsigned xcd_local_item(unsigned i, unsigned n) {
+  const unsigned per = n / kXcds;
+  return i < per * kXcds ? (i % kXcds) * per + i / kXcds : i;
+}
+
 // ---------------------------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------------------------

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SP == 16 ? 
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
-  const int bh = blockIdx.x;
+  const int bh = (int)xcd_local_item(blockIdx.x, gridDim.x);   // the heads of a B/C group share an L2
   const int b = bh / a.H, h = bh % a.H;
   if (a.active && !a.active[b]) return;   // uniform per work-group
   const int g = (int)(((int64_t)h * a.G) / a.H);
