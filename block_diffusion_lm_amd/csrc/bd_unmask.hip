@@ -96,21 +96,22 @@ __device__ __forceinline__ float load_logit(const void* row, int is_bf16, int64_
   return reinterpret_cast<const float*>(row)[j];
 }
 
-// The slice partials of row r combined in slice order; eight slices' loads are issued together.
+// The slice partials of row r combined in slice order; sixteen slices' loads are issued together.
 __device__ __forceinline__ Red row_partials(const UnmaskArgs& a, int64_t r) {
+  constexpr int U = 16;
   const float* pp = a.part + r * a.vsplit * 3;
   Red st{-INFINITY, 0x7fffffff, 0.f};
-  for (int c0 = 0; c0 < a.vsplit; c0 += 8) {
-    float m[8], x[8], z[8];
+  for (int c0 = 0; c0 < a.vsplit; c0 += U) {
+    float m[U], x[U], z[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < U; ++j) {
       const int c = min(c0 + j, a.vsplit - 1);   // past the last slice: reloaded, then skipped
       m[j] = pp[3 * c];
       x[j] = pp[3 * c + 1];
       z[j] = pp[3 * c + 2];
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < U; ++j)
       if (c0 + j < a.vsplit) st = combine(st, Red{m[j], __float_as_int(x[j]), z[j]});
   }
   return st;
@@ -205,11 +206,14 @@ __device__ void commit_sequence(const UnmaskArgs& a, int b) {
   const int s = threadIdx.x & 63;
   const bool in = s < a.S;
   const int64_t r = (int64_t)b * a.S + s;
+  // the row's slice partials are loaded together with its mask byte (in bounds for every row of
+  // the block; an unmasked row's are stale and dropped), so the commit waits for one round trip
+  Red st{-INFINITY, 0x7fffffff, 0.f};
+  if (in) st = row_partials(a, r);
   const bool masked = in && a.mask[r] != 0;
   float p = 0.f;
   int tok = -1;
   if (masked) {
-    const Red st = row_partials(a, r);
     p = 1.0f / st.z;
     tok = st.idx;
   }
