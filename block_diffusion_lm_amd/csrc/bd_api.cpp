@@ -145,12 +145,13 @@ bd_status plan_attn(const bd_attn_desc* d, bd::AttnPlan* p) {
   p->direct = p->nsplit == 1;
   p->wide_merge = p->nsplit > 16;
   if (p->direct) {
-    p->part_o_off = p->part_ml_off = p->bytes = 0;
+    p->part_o_off = p->part_ml_off = p->plan_off = p->bytes = 0;
   } else {
     const size_t prow = (size_t)p->n_items * tile_rows;
     p->part_o_off = 0;
     p->part_ml_off = align_up(prow * d->head_dim * sizeof(uint16_t), 256);
-    p->bytes = align_up(p->part_ml_off + prow * 2 * sizeof(float), 256);
+    p->plan_off = align_up(p->part_ml_off + prow * 2 * sizeof(float), 256);
+    p->bytes = align_up(p->plan_off + ((size_t)d->batch + 1) * sizeof(int32_t), 256);
   }
   const int64_t merge_rows = (int64_t)d->batch * d->n_kv_heads * p->rows;
   if (merge_rows > 0x7fffffff || p->n_items * p->waves * 64 > (int64_t)0xffffffff)
@@ -191,6 +192,7 @@ bd_status run_attn(const bd_attn_desc* d, const bd::AttnPlan& plan, const void* 
   char* w = static_cast<char*>(ws);
   a.part_o = plan.direct ? nullptr : reinterpret_cast<uint16_t*>(w + plan.part_o_off);
   a.part_ml = plan.direct ? nullptr : reinterpret_cast<float*>(w + plan.part_ml_off);
+  a.plan_pfx = plan.direct ? nullptr : reinterpret_cast<int*>(w + plan.plan_off);
   a.B = d->batch;
   a.S = d->block_len;
   a.Hq = d->n_q_heads;
@@ -206,6 +208,7 @@ bd_status run_attn(const bd_attn_desc* d, const bd::AttnPlan& plan, const void* 
   const float tau = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
   a.scale_log2 = tau * 1.4426950408889634f;
   a.direct = plan.direct ? 1 : 0;
+  a.balanced = !plan.direct && d->batch <= bd::kMaxBalancedBatch ? 1 : 0;
   a.causal = d->causal;
   bd_status st = traced("attn_split", stream, [&](const bd::Launch& l) { return bd::launch_attn_split(plan, a, l); });
   if (st != BD_OK || plan.direct) return st;

@@ -187,6 +187,172 @@ struct ActiveScan {
   }
 };
 
+// Work-group sums and maximum of three values (every thread takes part; results uniform).
+template <int NT>
+__device__ __forceinline__ void wg_reduce3(int64_t& sum, int& mx, int& cnt, int64_t* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    sum += __shfl_xor(sum, m, 64);
+    mx = max(mx, __shfl_xor(mx, m, 64));
+    cnt += __shfl_xor(cnt, m, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[3 * (threadIdx.x >> 6)] = sum;
+    red[3 * (threadIdx.x >> 6) + 1] = mx;
+    red[3 * (threadIdx.x >> 6) + 2] = cnt;
+  }
+  __syncthreads();
+  sum = 0;
+  mx = 0;
+  cnt = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    sum += red[3 * w];
+    mx = max(mx, (int)red[3 * w + 1]);
+    cnt += (int)red[3 * w + 2];
+  }
+  __syncthreads();
+}
+
+// Length-balanced plan of a split launch (B <= kMaxBalancedBatch, no direct plan). With
+// x_b = prefix_len[b] + S keys for an active sequence b (0 otherwise), every active sequence gets
+// ns_b = ceil(x_b / C) chunks of C keys, C the smallest multiple of 64 for which all of them fit
+// the launch's K = B * nsplit chunk slots per (KV head, row tile); sequence b's chunks take slots
+// pfx[b] .. pfx[b + 1] - 1 (pfx: exclusive prefix sums of ns_b in sequence order, pfx[B] the total).
+// Ragged lengths then get chunks of the size the total work calls for instead of the longest
+// sequence's, and a length above the host's bound still gets all its keys. C is found by bisection
+// between lower bound ceil(total / K) (feasible at once when the lengths are equal) and
+// min(total / (K - n_act), max_b x_b), both feasible; every work-group of the split and of the
+// merge launch computes the same plan from the same inputs.
+struct BalancedPlan {
+  int64_t chunk;   // C
+  int total;       // sum of ns_b
+};
+
+template <int NT>
+__device__ BalancedPlan balanced_plan(const AttnArgs& a, int* pfx, int64_t* red) {
+  constexpr int NR = (kMaxBalancedBatch + NT - 1) / NT;
+  const int tid = threadIdx.x;
+  uint32_t x[NR];
+  int64_t tot = 0;
+  int mx = 0, nact = 0;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int b = tid + NT * i;
+    const bool on = b < a.B && (!a.active || a.active[b]);
+    x[i] = on ? (uint32_t)a.prefix_len[b] + (uint32_t)a.S : 0u;   // (no load past B)
+    tot += x[i];
+    mx = max(mx, (int)x[i]);
+    nact += on ? 1 : 0;
+  }
+  wg_reduce3<NT>(tot, mx, nact, red);
+  BalancedPlan p{64, 0};
+  if (nact == 0) return p;
+  const int64_t K = (int64_t)a.B * a.nsplit;
+  auto fits = [&](uint32_t c) {
+    int64_t n = 0;
+    int unused_m = 0, unused_c = 0;
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      if (x[i]) n += (x[i] + c - 1) / c;
+    wg_reduce3<NT>(n, unused_m, unused_c, red);
+    return n <= K;
+  };
+  int64_t lo = max((int64_t)1, (tot + 64 * K - 1) / (64 * K));                 // in 64-key units
+  const int64_t hi_a = (tot + 64 * (K - nact) - 1) / (64 * (K - nact));       // K > nact: nsplit >= 2
+  int64_t hi = max(lo, min(hi_a, ((int64_t)mx + 63) / 64));
+  if (!fits((uint32_t)(lo * 64))) {
+    while (hi - lo > 1) {   // lo infeasible, hi feasible
+      const int64_t mid = (lo + hi) / 2;
+      if (fits((uint32_t)(mid * 64))) hi = mid;
+      else lo = mid;
+    }
+    lo = hi;
+  }
+  const uint32_t c = (uint32_t)(lo * 64);
+  p.chunk = c;
+  // exclusive prefix sums of ns_b in sequence order, NT sequences a round
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    if (NT * i >= a.B) break;   // uniform
+    const int v = (int)((x[i] + c - 1) / c);
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(inc, d, 64);
+      if ((tid & 63) >= d) inc += o;
+    }
+    if ((tid & 63) == 63) red[tid >> 6] = inc;
+    __syncthreads();
+    int before = base, round = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      const int t = (int)red[w];
+      if (w < (tid >> 6)) before += t;
+      round += t;
+    }
+    const int b = tid + NT * i;
+    if (b < a.B) pfx[b] = before + inc - v;
+    base += round;
+    __syncthreads();
+  }
+  if (tid == 0) pfx[a.B] = base;
+  __syncthreads();
+  p.total = base;
+  return p;
+}
+
+// The same plan for B <= 64, computed by one wave on its own (lane = sequence): wave-wide sums by
+// shuffles, no LDS and no barrier, so every wave of a work-group derives it independently. The sums
+// fit 32 bits (64 sequences of at most 2^23 + 64 keys: prefix capacity check). Lane b receives its
+// first chunk slot (pfx) and its chunk count (ns).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ BalancedPlan balanced_plan_wave(const AttnArgs& a, int& pfx, int& ns) {
+  const int lane = threadIdx.x & 63;
+  const bool on = lane < a.B && (!a.active || a.active[lane]);
+  const uint32_t x = on ? (uint32_t)a.prefix_len[lane] + (uint32_t)a.S : 0u;
+  const uint32_t tot = wave_sum(x);
+  uint32_t mx = x;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, m, 64));
+  const int nact = __popcll(__builtin_amdgcn_ballot_w64(on));
+  BalancedPlan p{64, 0};
+  pfx = 0;
+  ns = 0;
+  if (nact == 0) return p;
+  const uint32_t K = (uint32_t)a.B * (uint32_t)a.nsplit;   // <= 64 * nsplit
+  auto fits = [&](uint32_t c) { return wave_sum(x ? (x + c - 1) / c : 0u) <= K; };
+  uint32_t lo = max(1u, (tot + 64 * K - 1) / (64 * K));
+  const uint32_t hi_a = (tot + 64 * (K - nact) - 1) / (64 * (K - nact));
+  uint32_t hi = max(lo, min(hi_a, (mx + 63) / 64));
+  if (!fits(lo * 64)) {
+    while (hi - lo > 1) {
+      const uint32_t mid = (lo + hi) / 2;
+      if (fits(mid * 64)) hi = mid;
+      else lo = mid;
+    }
+    lo = hi;
+  }
+  const uint32_t c = lo * 64;
+  p.chunk = c;
+  ns = (int)(x ? (x + c - 1) / c : 0u);
+  int inc = ns;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += o;
+  }
+  pfx = inc - ns;
+  p.total = __shfl(inc, 63, 64);
+  return p;
+}
+
 template <int D>
 struct Geo {
   static constexpr int KT = kAttnKeyTile;           // keys per LDS tile
@@ -313,8 +479,6 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
   static_assert(NK * NWD == G::JK && NV * NWD == JV && NWD % 2 == 0, "copies split evenly over the copying waves");
   static_assert(NMIN * 3 < 64 && NSTAGE <= 5, "vmcnt range");
 
-  __shared__ __attribute__((aligned(16))) char smem[NSTAGE * G::STAGE];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches and bases
@@ -327,22 +491,70 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
   if ((nitems & 7) == 0) item = (item & 7) * (nitems >> 3) + (item >> 3);
   // (values loaded from memory are made explicitly wave-uniform, so that the tile bookkeeping
   // and the DMA bases below live in scalar registers)
+  __shared__ __attribute__((aligned(16))) char smem[NSTAGE * G::STAGE];
   __shared__ uint64_t act_masks[NW];
-  ActiveScan<NT> scan{act_masks};
-  const int n_act = __builtin_amdgcn_readfirstlane(scan.count(a.active, a.B));
-  const ItemMap im = device_plan(a, n_act);
+  __shared__ int64_t red[3 * NW];
+  __shared__ int found_b;
   const int rt = (int)(item % a.row_tiles);
-  const int64_t ps = item / a.row_tiles;
-  const int split = (int)(ps % im.nsplit);
-  const int64_t pair_a = ps / im.nsplit;              // pair among the active sequences
-  if (pair_a >= (int64_t)n_act * a.Hkv) return;
-  const int b = __builtin_amdgcn_readfirstlane(scan.nth(a.active, a.B, (int)(pair_a / a.Hkv)));
-  const int g = (int)(pair_a % a.Hkv);
+  int b, g, nsplit_out;
+  int64_t k_begin, k_end, item_out;   // item_out: where the partials go (merge layout)
+  if (a.balanced) {
+    // slot j of KV head g and the sequence whose chunks hold it; the first work-group also stores
+    // the plan's prefix sums for the merge
+    const int64_t q = item / a.row_tiles;
+    g = (int)(q % a.Hkv);
+    const int j = (int)(q / a.Hkv);
+    BalancedPlan bp;
+    int c;
+    if (a.B <= 64) {
+      int pfx_l, ns_l;
+      bp = balanced_plan_wave(a, pfx_l, ns_l);
+      if (blockIdx.x == 0 && wave == 0) {
+        if (lane < a.B) a.plan_pfx[lane] = pfx_l;
+        if (lane == 0) a.plan_pfx[a.B] = bp.total;
+      }
+      if (j >= bp.total) return;   // uniform
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(ns_l > 0 && pfx_l <= j && j < pfx_l + ns_l);
+      b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+      c = j - __builtin_amdgcn_readfirstlane(__shfl(pfx_l, b, 64));
+    } else {
+      // pfx lives in the tile ring until the first copy; every wave has read it before the barrier
+      int* pfx = reinterpret_cast<int*>(smem);
+      bp = balanced_plan<NT>(a, pfx, red);
+      if (blockIdx.x == 0)
+        for (int bb = tid; bb <= a.B; bb += NT) a.plan_pfx[bb] = pfx[bb];
+      if (j >= bp.total) return;   // uniform
+      for (int bb = tid; bb < a.B; bb += NT)
+        if (pfx[bb] <= j && j < pfx[bb + 1]) found_b = bb;
+      __syncthreads();
+      b = __builtin_amdgcn_readfirstlane(found_b);
+      c = j - pfx[b];
+      __syncthreads();
+    }
+    const int64_t nkeys = (int64_t)__builtin_amdgcn_readfirstlane(a.prefix_len[b]) + a.S;
+    k_begin = (int64_t)c * bp.chunk;
+    k_end = min(k_begin + bp.chunk, nkeys);
+    item_out = ((int64_t)j * a.Hkv + g) * a.row_tiles + rt;
+    nsplit_out = 2;   // partials always (no direct plan here)
+  } else {
+    ActiveScan<NT> scan{act_masks};
+    const int n_act = __builtin_amdgcn_readfirstlane(scan.count(a.active, a.B));
+    const ItemMap im = device_plan(a, n_act);
+    const int64_t ps = item / a.row_tiles;
+    const int split = (int)(ps % im.nsplit);
+    const int64_t pair_a = ps / im.nsplit;              // pair among the active sequences
+    if (pair_a >= (int64_t)n_act * a.Hkv) return;
+    b = __builtin_amdgcn_readfirstlane(scan.nth(a.active, a.B, (int)(pair_a / a.Hkv)));
+    g = (int)(pair_a % a.Hkv);
+    const int64_t nkeys = (int64_t)__builtin_amdgcn_readfirstlane(a.prefix_len[b]) + a.S;
+    k_begin = (int64_t)split * im.chunk;
+    // a direct plan (one chunk) takes every key of the sequence
+    k_end = a.direct ? nkeys : min(k_begin + im.chunk, nkeys);
+    item_out = (pair_a * im.nsplit + split) * a.row_tiles + rt;
+    nsplit_out = im.nsplit;
+  }
+  if (k_begin >= k_end) return;
   const int64_t len = __builtin_amdgcn_readfirstlane(a.prefix_len[b]);
-  const int64_t nkeys = len + a.S;
-  const int64_t k_begin = (int64_t)split * im.chunk;
-  if (k_begin >= nkeys) return;
-  const int64_t k_end = min(k_begin + im.chunk, nkeys);
   const int ntiles = (int)((k_end - k_begin + G::KT - 1) / G::KT);
 
   const int tile_rows = NW * RB * 32;
@@ -771,7 +983,6 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
   if (!wave_rows) return;
 
   // ---- epilogue: lane owns row lrow of each row block; dims db*32 + 8*(r/4) + 4*half + r%4
-  const int64_t item_act = (pair_a * im.nsplit + split) * a.row_tiles + rt;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float l_tot = l_run[rb] + other_half(l_run[rb]);
@@ -779,7 +990,7 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
     if (r >= a.rows) continue;
     const int s = r / a.group;
     const int hq = g * a.group + (r - s * a.group);
-    if (im.nsplit == 1) {
+    if (nsplit_out == 1) {
       const float inv = 1.0f / l_tot;
       uint16_t* op = a.out + (((int64_t)b * a.S + s) * a.Hq + hq) * D;
 #pragma unroll
@@ -796,7 +1007,7 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
     } else {
       // partial of this chunk: (m, l) and the normalized output acc / l in bf16 (zero for a chunk
       // without a visible key); merged by the merge kernel
-      const int64_t prow = item_act * tile_rows + (r - rt * tile_rows);
+      const int64_t prow = item_out * tile_rows + (r - rt * tile_rows);
       const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
       uint16_t* ap = a.part_o + prow * D;
 #pragma unroll
@@ -859,47 +1070,74 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int tile_ro
     r[k] = live ? (int)(rowg - pair * (uint32_t)a.rows) : 0;
     b[k] = (int)(pair / (uint32_t)a.Hkv);
     g[k] = (int)(pair - (uint32_t)b[k] * a.Hkv);
-    // the sequence's length first: it is needed last (to drop the chunks past its keys), and its
-    // load then overlaps the scan of the active flags and the partial loads
-    plen[k] = live ? a.prefix_len[b[k]] : 0;
+    // (uniform plan) the sequence's length first: it is needed last (to drop the chunks past its
+    // keys), and its load then overlaps the scan of the active flags and the partial loads
+    plen[k] = live && !a.balanced ? a.prefix_len[b[k]] : 0;
     act[k] = live && !(a.active && !a.active[b[k]]);
   }
-  __shared__ uint64_t act_masks[4];
-  ActiveScan<256> scan{act_masks};
-  int n_act, rank_b[RPT];   // every thread takes part in the scan's barriers
-  scan.count_ranks<RPT>(a.active, a.B, b, n_act, rank_b);
-  const ItemMap im = device_plan(a, n_act);
-  if (im.nsplit == 1) return;   // the split kernel wrote the output itself
-  const int64_t pstride = (int64_t)a.row_tiles * tile_rows;   // partial rows between chunks
+  // where row k's chunk partials are (p0[k] + c * pstride, c < nclamp[k]) under either plan; an
+  // inactive row reads the workspace's first rows (in bounds, shared by all such rows) and drops
+  // them: no branch around the loads
+  ItemMap im{a.nsplit, a.chunk};
+  int64_t pstride;
   int64_t p0[RPT];
+  int nclamp[RPT];
+  int nl = 0;   // chunk slots this thread walks
+  if (a.balanced) {
+    // the split launch's plan (its first work-group stored the prefix sums)
+    pstride = (int64_t)a.Hkv * a.row_tiles * tile_rows;   // partial rows between chunks
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      p0[k] = 0;
+      nclamp[k] = 0;
+      if (act[k]) {
+        const int P = a.plan_pfx[b[k]];
+        nclamp[k] = a.plan_pfx[b[k] + 1] - P;   // every chunk of the sequence holds keys
+        const int rt = r[k] / tile_rows;
+        p0[k] = (((int64_t)P * a.Hkv + g[k]) * a.row_tiles + rt) * tile_rows + (r[k] - rt * tile_rows);
+      }
+      nl = max(nl, nclamp[k]);
+    }
+  } else {
+    __shared__ uint64_t act_masks[4];
+    ActiveScan<256> scan{act_masks};
+    int n_act, rank_b[RPT];   // every thread takes part in the scan's barriers
+    scan.count_ranks<RPT>(a.active, a.B, b, n_act, rank_b);
+    im = device_plan(a, n_act);
+    if (im.nsplit == 1) return;   // the split kernel wrote the output itself
+    pstride = (int64_t)a.row_tiles * tile_rows;
+    nl = im.nsplit;
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      p0[k] = 0;
+      nclamp[k] = im.nsplit;
+      if (act[k]) {
+        const int64_t pair_a = (int64_t)rank_b[k] * a.Hkv + g[k];
+        const int rt = r[k] / tile_rows;
+        p0[k] = ((pair_a * im.nsplit) * a.row_tiles + rt) * tile_rows + (r[k] - rt * tile_rows);
+      }
+    }
+  }
   int ns[RPT];
   float M[RPT], den[RPT];
   f32x4 num[RPT];
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
-    // an inactive row reads the workspace's first rows (in bounds, shared by all such rows) and
-    // drops them: no branch around the loads
-    p0[k] = 0;
-    if (act[k]) {
-      const int64_t pair_a = (int64_t)rank_b[k] * a.Hkv + g[k];
-      const int rt = r[k] / tile_rows;
-      p0[k] = ((pair_a * im.nsplit) * a.row_tiles + rt) * tile_rows + (r[k] - rt * tile_rows);
-    }
     M[k] = -INFINITY;
     den[k] = 0.f;
     num[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  for (int c0 = cg; c0 < im.nsplit; c0 += U * CG) {
+  for (int c0 = cg; c0 < nl; c0 += U * CG) {
     float mm[RPT][U], ll[RPT][U];
     f32x4 v[RPT][U];
-    // every slot loads a chunk of the plan (past the plan's last: the last again), so that all the
+    // every slot loads a chunk of the plan (past the row's last: the last again), so that all the
     // loads of the round are issued before the first is used and before the lengths are known;
-    // chunks past a sequence's keys were not written by this call and are dropped here
+    // chunks past a sequence's keys (uniform plan) were not written by this call and are dropped
 #pragma unroll
     for (int k = 0; k < RPT; ++k)
 #pragma unroll
       for (int j = 0; j < U; ++j) {
-        const int c = min(c0 + j * CG, im.nsplit - 1);
+        const int c = min(c0 + j * CG, max(nclamp[k] - 1, 0));
         const int64_t pr = p0[k] + c * pstride;
         const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
         mm[k][j] = ml.x;
@@ -911,7 +1149,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int tile_ro
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const uint32_t chunk = (uint32_t)im.chunk;   // <= max_prefix_len + S < 2^31
-      ns[k] = act[k] ? (int)min((uint32_t)im.nsplit, (plen[k] + a.S + chunk - 1) / chunk) : 0;
+      ns[k] = !act[k] ? 0 : a.balanced ? nclamp[k] : (int)min((uint32_t)im.nsplit, (plen[k] + a.S + chunk - 1) / chunk);
 #pragma unroll
       for (int j = 0; j < U; ++j)
         if (c0 + j * CG >= ns[k]) {

@@ -59,7 +59,7 @@ struct AttnPlan {
   int64_t n_items;    // B * Hkv * nsplit * row_tiles workgroups
   bool direct;        // nsplit == 1: the split kernel writes the final output itself
   bool wide_merge;    // many splits: the merge spreads each row's chunks over eight thread groups
-  size_t part_o_off, part_ml_off, bytes;   // workspace layout
+  size_t part_o_off, part_ml_off, plan_off, bytes;   // workspace layout
 };
 
 struct AttnArgs {
@@ -74,6 +74,8 @@ struct AttnArgs {
   float* lse;
   uint16_t* part_o;   // [n_items][rows_pad][D] bf16: the chunk's normalized output acc / l
   float* part_ml;     // [n_items][rows_pad][2]: running max (log2 units) and sum
+  int* plan_pfx;      // [B + 1] balanced plan: first chunk slot of every sequence, then the total
+                      // (written by the split launch's first work-group, read by the merge)
   int B, S, Hq, Hkv, group, rows, rows_pad;
   int64_t lcap;
   int64_t chunk;
@@ -81,8 +83,14 @@ struct AttnArgs {
   int nsplit, row_tiles;
   float scale_log2;   // tau * log2(e)
   int direct;
+  int balanced;       // split launch over at most kMaxBalancedBatch sequences: chunks sized on the
+                      // device from the actual lengths (see balanced_plan in bd_attn.hip)
   int causal;         // 1: block key j is visible to block position s only when j <= s
 };
+
+// Largest batch whose split launches plan their chunks from the actual prefix lengths on the device
+// (the work-groups keep one prefix-sum entry per sequence in LDS).
+constexpr int kMaxBalancedBatch = 1024;
 
 hipError_t launch_attn_split(const AttnPlan& plan, const AttnArgs& a, const Launch& l);
 hipError_t launch_attn_merge(const AttnPlan& plan, const AttnArgs& a, const Launch& l);
