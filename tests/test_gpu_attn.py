@@ -197,6 +197,57 @@ def test_tile_edges_of_the_long_prefix_kernel(lens, D, num_splits, causal):
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
 
 
+RAGGED = [
+    # name, Hq, Hkv, D, lengths: one long sequence among very short ones (the plan sizes chunks
+    # from the actual lengths: the long one takes most of the slots), empty prefixes, tile edges
+    ("ragged-wave-plan", 8, 2, 128, (32768, 1, 0, 5, 4097, 64, 63, 20000, 2)),
+    ("ragged-d64", 16, 4, 64, (0, 0, 9000, 0, 1, 129)),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[c[0] for c in RAGGED])
+@pytest.mark.parametrize("num_splits", [0, 3, 7])
+@pytest.mark.parametrize("causal", [False, True])
+def test_length_balanced_plan(case, num_splits, causal):
+    """Split launches plan their chunks from the actual prefix lengths on the device: every row of
+    a very ragged batch against the oracle (forced and automatic split counts, both modes)."""
+    name, Hq, Hkv, D, lens = case
+    lens = np.asarray(lens, np.int32)
+    w = I.small_workload(name, B=len(lens), Hq=Hq, Hkv=Hkv, D=D, S=16, prefix_len=int(lens.max()),
+                         wid=370 + RAGGED.index(case))
+    plan = bd.attn_plan(bd.attn_desc(w.B, Hq, Hkv, D, 16, int(lens.max()), int(lens.max()), num_splits=num_splits,
+                                     causal=causal))
+    assert plan["num_splits"] > 1, plan
+    inp = I.attn_inputs(w, lens=lens)
+    print(f"[attn] {name} splits={num_splits} causal={causal} plan={plan}", flush=True)
+    got, lse, _ = run_gpu(inp, num_splits=num_splits, causal=causal)
+    ref, ref_lse = oracle_attn_all(inp, causal=causal)
+    assert_attn_close(got, ref, name)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
+
+
+@pytest.mark.parametrize("B,num_splits", [(5, 2), (5, 4), (80, 2), (80, 3), (5, 1), (80, 1)],
+                         ids=["wave-plan-2", "wave-plan-4", "group-plan-2", "group-plan-3", "one-chunk-5",
+                              "one-chunk-80"])
+def test_lengths_above_the_host_bound(B, num_splits):
+    """prefix_len above the descriptor's max_prefix_len (but within the cache): the device plan (per
+    wave up to 64 sequences, per work-group beyond) and the one-chunk plan still take every key of
+    every sequence, so the output matches the oracle over the true lengths."""
+    rng = np.random.default_rng(380 + B + num_splits)
+    lens = rng.integers(0, 1500, size=B).astype(np.int32)
+    lens[0] = 1500
+    w = I.small_workload(f"over-bound-{B}", B=B, Hq=8, Hkv=2, D=64, S=16, prefix_len=2048, wid=381 + B)
+    inp = I.attn_inputs(w, lens=lens)
+    bound = 100   # the host's (stale) bound: far below the true lengths
+    plan = bd.attn_plan(bd.attn_desc(B, 8, 2, 64, 16, 2048, bound, num_splits=num_splits))
+    assert (plan["num_splits"] > 1) == (num_splits > 1), plan
+    print(f"[attn] over-bound B={B} splits={num_splits} plan={plan}", flush=True)
+    got, lse, _ = run_gpu(inp, num_splits=num_splits, max_prefix_len=bound)
+    ref, ref_lse = oracle_attn_all(inp)
+    assert_attn_close(got, ref, f"over-bound-{B}")
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
+
+
 MANY = [
     # name, Hq, Hkv, D, num_splits, waves: 512 sequences; 64 and 128 rows per KV head plan the
     # four-wave kernel (with 64 rows half its waves hold no rows), 256 rows the eight-wave one;
