@@ -11,6 +11,9 @@
 // thread 0 advances prefix_len[b] by S. Larger blocks take two: kv_append, one thread per 16 bytes
 // of a (sequence, block position, KV head) row of K and of V over the whole grid, then
 // len_advance (a second launch, so no thread reads a length another has already advanced).
+// A sequence whose length breaks the precondition (negative, or prefix_len[b] + S above the
+// capacity) is skipped by all three kernels: nothing written, its length not advanced, so a stale
+// host bound cannot write into another sequence's rows or past the cache.
 #include "bd_internal.h"
 
 namespace bd {
@@ -29,7 +32,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   const int s = (int)((row / a.Hkv) % a.S);
   const int b = (int)(row / ((int64_t)a.Hkv * a.S));
   if (a.active && !a.active[b]) return;
-  const int64_t pos = (int64_t)a.prefix_len[b] + s;
+  const int64_t len = a.prefix_len[b];
+  if (len < 0 || len + a.S > a.lcap) return;
+  const int64_t pos = len + s;
   const int64_t src = row * a.D + d8 * 8;
   const int64_t dst = (((int64_t)b * a.Hkv + g) * a.lcap + pos) * a.D + d8 * 8;
   *reinterpret_cast<u32x4*>(a.k_cache + dst) = *reinterpret_cast<const u32x4*>(a.k_new + src);
@@ -44,6 +49,7 @@ __global__ __launch_bounds__(256) void kv_append_seq_kernel(AppendArgs a) {
   const int D8 = a.D / 8;
   const int units = a.S * a.Hkv * D8;     // <= 256 * U
   const int64_t len = a.prefix_len[b];
+  if (len < 0 || len + a.S > a.lcap) return;   // uniform per workgroup
   u32x4 k[U], v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -72,7 +78,9 @@ __global__ __launch_bounds__(256) void kv_append_seq_kernel(AppendArgs a) {
 
 __global__ __launch_bounds__(64) void len_advance_kernel(AppendArgs a) {
   const int b = blockIdx.x * 64 + threadIdx.x;
-  if (b < a.B && (!a.active || a.active[b])) a.prefix_len[b] += a.S;
+  if (b >= a.B || (a.active && !a.active[b])) return;
+  const int64_t len = a.prefix_len[b];
+  if (len >= 0 && len + a.S <= a.lcap) a.prefix_len[b] = (int32_t)(len + a.S);
 }
 
 }  // namespace

@@ -157,7 +157,10 @@ bd_status bd_attn_step(const bd_attn_desc* desc,
  * desc: the attention descriptor (batch, n_kv_heads, head_dim, block_len = S, prefix_capacity,
  *       max_prefix_len); max_prefix_len + S must not exceed prefix_capacity (BD_EINVAL otherwise),
  *       and prefix_len[b] <= max_prefix_len is the device-side precondition as for bd_attn_step.
- *       Afterwards max_prefix_len + S bounds the new lengths.
+ *       Afterwards max_prefix_len + S bounds the new lengths. A sequence that breaks the device
+ *       precondition so far that prefix_len[b] + S would pass prefix_capacity (or whose length is
+ *       negative) is left untouched: no row written, prefix_len[b] not advanced (the caller sees it
+ *       in prefix_len).
  * k_new, v_new: bf16 [B, S, Hkv, D] (read only); k_cache, v_cache: bf16 [B, Hkv, Lcap, D] (rows
  *       prefix_len[b] .. prefix_len[b]+S-1 written); prefix_len: int32 [B] (read, then advanced);
  * active: uint8 [B] or NULL (all). Inactive sequences are untouched. No workspace. */

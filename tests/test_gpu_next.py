@@ -139,6 +139,28 @@ def test_kv_append_fills_the_cache_exactly():
     np.testing.assert_array_equal(ln.cpu().numpy(), rl)
 
 
+@pytest.mark.parametrize("S,Hkv", [(16, 2), (64, 4)], ids=["one-launch", "two-launches"])
+def test_kv_append_skips_a_length_past_the_capacity(S, Hkv):
+    """A stale host bound: sequence 0's device length leaves fewer than S free rows. Its slab and
+    length stay as they were (nothing lands in sequence 1's slab), the other sequences append as
+    usual. Both the one-launch and the two-launch path."""
+    w = I.small_workload("append-guard", B=3, Hq=4 * Hkv, Hkv=Hkv, D=128, S=S, prefix_len=(20, 100), wid=329 + S)
+    lens = I.prefix_lengths(w)
+    cache = capacity_cache(w, lens, S)   # capacity: longest prefix + S
+    cap = cache["k_cache"].shape[2]
+    lens = lens.copy()
+    lens[0] = cap - S + 1                # one row short
+    new = I.attn_inputs(w, lens=lens, cache=False)
+    kc, vc, ln = dev_bf16(cache["k_cache"]), dev_bf16(cache["v_cache"]), dev(lens.copy())
+    bd.kv_append(dev_bf16(new["k_blk"]), dev_bf16(new["v_blk"]), kc, vc, ln, max_prefix_len=cap - S)
+    torch.cuda.synchronize()
+    act = np.array([0, 1, 1], np.uint8)   # what must have happened: sequence 0 skipped
+    rk, rv, rl = O.kv_append(cache["k_cache"], cache["v_cache"], lens, new["k_blk"], new["v_blk"], act)
+    np.testing.assert_array_equal(kc.view(torch.int16).cpu().numpy().view(np.uint16), rk)
+    np.testing.assert_array_equal(vc.view(torch.int16).cpu().numpy().view(np.uint16), rv)
+    np.testing.assert_array_equal(ln.cpu().numpy(), rl)
+
+
 def test_commit_then_next_step_sees_the_appended_block():
     # causal pass + append of block 1, then the next block's denoise-step attention over the grown
     # cache equals the oracle's (its prefix now ends with block 1).
