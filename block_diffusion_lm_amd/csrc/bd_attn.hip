@@ -71,6 +71,13 @@ __device__ __forceinline__ float other_half(float x) {
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// a wave-uniform 64-bit value into scalar registers
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Device-side plan of one launch: which (sequence, KV head, chunk, row tile) a workgroup owns.
 // With every sequence active this is the host plan. With n_act < B active sequences the same
 // number of workgroups is spread over the active ones: splits per (sequence, KV head) grow to
@@ -553,6 +560,12 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
     item_out = (pair_a * im.nsplit + split) * a.row_tiles + rt;
     nsplit_out = im.nsplit;
   }
+  // the plan's values are wave-uniform (the balanced plan derives them with shuffles, in vector
+  // registers): keep them in scalar registers for the rest of the kernel
+  k_begin = uniform64(k_begin);
+  k_end = uniform64(k_end);
+  item_out = uniform64(item_out);
+  nsplit_out = __builtin_amdgcn_readfirstlane(nsplit_out);
   if (k_begin >= k_end) return;
   const int64_t len = __builtin_amdgcn_readfirstlane(a.prefix_len[b]);
   const int ntiles = (int)((k_end - k_begin + G::KT - 1) / G::KT);
