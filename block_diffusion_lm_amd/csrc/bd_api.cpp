@@ -280,6 +280,7 @@ bd_status run_unmask(const bd_unmask_desc* d, const bd::UnmaskPlan& plan, const 
   a.min_commit = d->min_commit;
   a.commit_all = commit_all;
   a.part = static_cast<float*>(ws);
+  a.compact = (int64_t)d->batch * d->block_len <= bd::kCompactRows ? 1 : 0;
   a.vsplit = plan.vsplit;
   a.slice = plan.slice;
   a.step = step;

@@ -118,6 +118,7 @@ struct UnmaskArgs {
   float gamma;
   int min_commit, commit_all;
   float* part;         // [B*S][vsplit][3]: max, index (as int bits), sum of exp
+  int compact;         // the reduction's work-groups take the masked rows in order (B*S <= kCompactRows)
   int vsplit;
   int64_t slice;
   // loop bookkeeping (all optional)
@@ -131,6 +132,10 @@ struct UnmaskArgs {
 };
 
 hipError_t launch_vocab_reduce(const UnmaskArgs& a, const Launch& l);
+
+// Most rows (B * S) whose masked positions the reduction compacts: every work-group scans that
+// many mask bytes, 16 per thread.
+constexpr int kCompactRows = 4096;
 
 // Allocation-free unmasking: the slice partials live in a static device array of this many bytes
 // (one copy per device, held until the process ends) instead of a caller workspace.

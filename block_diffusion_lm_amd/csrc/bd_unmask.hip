@@ -83,8 +83,8 @@ __device__ __forceinline__ void fold(Red& st, const float (&x)[N], int base) {
     st.m = lm;
     st.idx = base + li;
   }
-  if (st.m == -INFINITY) return;
-  const float mneg = -st.m * kLog2e;
+  // all values so far -inf (then every x is -inf): exp2(-inf) adds nothing, without a branch
+  const float mneg = st.m == -INFINITY ? 0.f : -st.m * kLog2e;
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < N; ++i) acc += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, mneg));
@@ -117,29 +117,85 @@ __device__ __forceinline__ Red row_partials(const UnmaskArgs& a, int64_t r) {
   return st;
 }
 
+template <bool BF16>
 __device__ void reduce_slice(const UnmaskArgs& a, int64_t row, int part);
 __device__ void commit_sequence(const UnmaskArgs& a, int b);
 
-__global__ __launch_bounds__(256) void vocab_reduce_kernel(UnmaskArgs a) {
-  const int64_t row = blockIdx.x / a.vsplit;
-  const int part = (int)(blockIdx.x % a.vsplit);
-  if (!a.mask || a.mask[row]) reduce_slice(a, row, part);   // uniform per workgroup
+// Position of the j-th masked row (rows in order) among the first `rows` <= kCompactRows mask
+// bytes, or -1 when fewer are masked. Thread t looks at rows 16 t .. 16 t + 15 (loads issued
+// unconditionally, past the end clamped and ignored); counts are scanned over the work-group.
+// All threads take part (LDS, barriers); the result is uniform.
+__device__ int nth_masked_row(const uint8_t* mask, int rows, int j) {
+  __shared__ int wsum[4];
+  __shared__ int found;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint8_t mb[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) mb[k] = mask[min(16 * tid + k, rows - 1)];
+  uint32_t bits = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) bits |= (16 * tid + k < rows && mb[k] != 0) ? 1u << k : 0u;
+  const int cnt = __popc(bits);
+  int inc = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  if (tid == 0) found = -1;
+  __syncthreads();
+  int excl = inc - cnt;
+  for (int w = 0; w < wave; ++w) excl += wsum[w];
+  if (j >= excl && j < excl + cnt) {
+    uint32_t b = bits;
+    for (int q = j - excl; q > 0; --q) b &= b - 1;   // drop the lower set bits
+    found = 16 * tid + __builtin_ctz(b);
+  }
+  __syncthreads();
+  return found;
 }
 
+// Work-group w reduces slice w % vsplit of row w / vsplit -- with `compact`, of the (w / vsplit)-th
+// masked row instead, so that the busy work-groups are the first ones of the grid and spread evenly
+// over the CUs whatever the mask (with scattered masked rows the direct mapping leaves some CUs with
+// several busy work-groups and others with none).
+template <bool BF16>
+__global__ __launch_bounds__(256) void vocab_reduce_kernel(UnmaskArgs a) {
+  const int part = (int)(blockIdx.x % a.vsplit);
+  int64_t row = blockIdx.x / a.vsplit;
+  if (a.compact && a.mask && a.B * a.S <= 64) {
+    // one ballot per wave (lane = row), no LDS or barrier
+    const int lane = threadIdx.x & 63;
+    const int rows = a.B * a.S;
+    uint64_t bits = __builtin_amdgcn_ballot_w64(lane < rows && a.mask[min(lane, rows - 1)] != 0);
+    if ((int64_t)__popcll(bits) <= row) return;   // uniform
+    for (int q = (int)row; q > 0; --q) bits &= bits - 1;   // drop the lower set bits
+    row = __builtin_ctzll(bits);
+  } else if (a.compact && a.mask) {
+    row = nth_masked_row(a.mask, a.B * a.S, (int)row);
+    if (row < 0) return;   // uniform
+  } else if (a.mask && !a.mask[row]) {
+    return;   // uniform per workgroup
+  }
+  reduce_slice<BF16>(a, row, part);
+}
+
+template <bool BF16>
 __device__ void reduce_slice(const UnmaskArgs& a, int64_t row, int part) {
   const int tid = threadIdx.x;
   const int64_t v0 = (int64_t)part * a.slice;
   const int64_t v1 = min(v0 + a.slice, (int64_t)a.vocab);
   Red st{-INFINITY, 0x7fffffff, 0.f};
   if (v0 < v1) {
-    const int elt = a.is_bf16 ? 2 : 4;
+    constexpr int elt = BF16 ? 2 : 4;
     const char* rowp = reinterpret_cast<const char*>(a.logits) + row * a.row_stride * elt;
-    const int per = 16 / elt;                       // elements per 16-byte vector
+    constexpr int per = 16 / elt;                   // elements per 16-byte vector
     const int64_t nvec = (v1 - v0) / per;           // full vectors of the slice
     const u32x4* vp = reinterpret_cast<const u32x4*>(rowp + v0 * elt);
     // vectors t, t + 256, ... in order; four loads in flight at a time
     auto fold_vec = [&](const u32x4 u, int64_t i) {
-      if (a.is_bf16) {
+      if constexpr (BF16) {
         float x[8];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -174,7 +230,7 @@ __device__ void reduce_slice(const UnmaskArgs& a, int64_t row, int part) {
     for (; i < nvec; i += 256) fold_vec(__builtin_nontemporal_load(vp + i), i);
     // ragged tail of the slice (vocab not a multiple of the vector width)
     for (int64_t j = v0 + nvec * per + tid; j < v1; j += 256) {
-      float x[1] = {load_logit(rowp, a.is_bf16, j)};
+      float x[1] = {load_logit(rowp, BF16, j)};
       Red t{-INFINITY, 0x7fffffff, 0.f};
       fold<1>(t, x, (int)j);
       st = combine(st, t);
@@ -313,7 +369,8 @@ hipError_t unmask_static_scratch(void** ptr) {
 
 hipError_t launch_vocab_reduce(const UnmaskArgs& a, const Launch& l) {
   const int64_t blocks = (int64_t)a.B * a.S * a.vsplit;
-  return launch_kernel(vocab_reduce_kernel, dim3((unsigned)blocks), dim3(256), l, a);
+  if (a.is_bf16) return launch_kernel(vocab_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), l, a);
+  return launch_kernel(vocab_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), l, a);
 }
 
 hipError_t launch_commit(const UnmaskArgs& a, const Launch& l) {

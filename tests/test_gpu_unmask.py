@@ -173,6 +173,29 @@ def test_random_unmask_shapes(case):
     run_both(logits, bf16, mask, S, gamma, min_commit=min_commit, commit_all=commit_all, vocab=V)
 
 
+@pytest.mark.parametrize("B,S,frac", [(1, 64, 0.3), (2, 33, 0.3), (64, 64, 0.3), (64, 64, 0.002), (80, 64, 0.5),
+                                       (3, 16, 0.0)],
+                         ids=["64rows-ballot", "66rows-scan", "4096rows-scan", "4096rows-few", "5120rows-direct",
+                              "none-masked"])
+def test_scattered_masks_on_every_reduction_mapping(B, S, frac):
+    """Scattered masked rows under each way the reduction maps work-groups to rows: a ballot per
+    wave (at most 64 rows), a work-group scan of the mask (up to 4096 rows, also with only a few
+    masked), and the direct mapping beyond; no masked row at all. Against the oracle."""
+    V = 3000
+    for attempt in range(50):
+        rng = np.random.default_rng([960 + B + S, attempt])
+        x = (rng.standard_normal((B * S, V)) * 3).astype(np.float32)
+        rows = rng.random(B * S) < 0.33
+        x[rows, rng.integers(0, V, size=int(rows.sum()))] += 12.0
+        mask = (rng.random(B * S) < frac).astype(np.uint8)
+        logits = I.f32_to_bf16_bits(x)
+        ref = O.confidence_unmask(logits, mask, np.zeros(B * S, np.int32), S, 0.9, True, False, decode=O.bf16_to_f64)
+        if not O.near_ties(ref["conf"], mask, S, 0.9, True, False):
+            break
+    print(f"[unmask] scattered B={B} S={S} masked={int(mask.sum())}", flush=True)
+    run_both(logits, True, mask, S, 0.9, min_commit=True, commit_all=False, vocab=V)
+
+
 def test_vocabulary_beyond_2_pow_24():
     """A vocabulary past 2^24 (ragged, padded stride): argmax indices above 2^24 are exact (they
     travel as integers, never as float32), the lowest of two equal maxima wins up there too."""
