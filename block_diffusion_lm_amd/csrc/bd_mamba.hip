@@ -76,8 +76,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SP == 16 ? 
   const int wave = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
   const int bh = (int)xcd_local_item(blockIdx.x, gridDim.x);   // the heads of a B/C group share an L2
-  const int b = bh / a.H, h = bh % a.H;
-  if (a.active && !a.active[b]) return;   // uniform per work-group
+  const int h = bh % a.H;
+  int b = bh / a.H;
+  if (a.active && a.B <= 64) {
+    // the (bh / H)-th active sequence (one ballot per wave), so that the busy work-groups are the
+    // first ones of the grid and spread over every XCD whichever sequences have retired
+    const int ln = tid & 63;
+    uint64_t bits = __builtin_amdgcn_ballot_w64(ln < a.B && a.active[min(ln, a.B - 1)] != 0);
+    if (__popcll(bits) <= b) return;   // uniform
+    for (int q = b; q > 0; --q) bits &= bits - 1;   // drop the lower set bits
+    b = __builtin_ctzll(bits);
+  } else if (a.active && !a.active[b]) {
+    return;   // uniform per work-group
+  }
   const int g = (int)(((int64_t)h * a.G) / a.H);
   const int S = a.S;
   const int64_t row0 = (int64_t)b * S;   // (b, s = 0) row of the [B, S, ...] inputs

@@ -118,6 +118,30 @@ def test_mamba_inactive_sequences_and_no_h_out():
     assert torch.equal(y2[sel].view(torch.int16), y[sel].view(torch.int16))
 
 
+@pytest.mark.parametrize("B", [40, 70], ids=["ballot-40", "direct-70"])
+def test_mamba_scattered_active_sequences(B):
+    """A scattered active mask: up to 64 sequences the work-groups take the active ones in order
+    (one ballot per wave), beyond that they map directly; active sequences match the oracle,
+    retired ones keep y and h_out as they were."""
+    inp = I.mamba_inputs(520 + B, B, 16, 8, 2, 64)
+    act = (np.random.default_rng(521 + B).random(B) < 0.35).astype(np.uint8)
+    act[0], act[-1] = 0, 1
+
+    def dside(sd):
+        return (dev_bf16(sd["x"]), dev(sd["dt"]), dev_bf16(sd["Bm"]), dev_bf16(sd["Cm"]))
+    y = torch.full((B, 16, 8, 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    h_out = torch.full((B, 8, 64, 64), -7.0, dtype=torch.float32, device="cuda")
+    y0, h0c = y.clone(), h_out.clone()
+    print(f"[mamba] scattered active B={B} active={int(act.sum())}", flush=True)
+    bd.mamba_block_scan(dev(inp["h0"]), dside(inp["fwd"]), dside(inp["rev"]), dev(inp["fwd"]["A"]), dev(inp["rev"]["A"]),
+                        dev(inp["D"]), active=dev(act), y=y, h_out=h_out)
+    torch.cuda.synchronize()
+    off = torch.from_numpy(act == 0).cuda()
+    assert torch.equal(y[off].view(torch.int16), y0[off].view(torch.int16))
+    assert torch.equal(h_out[off], h0c[off])
+    check(inp, y, h_out, active=act)
+
+
 def test_mamba_in_place_state_update():
     """h_out = h0: the cache entry advanced in place gives the out-of-place results bit for bit."""
     inp = I.mamba_inputs(514, 4, 16, 16, 4, 128)
