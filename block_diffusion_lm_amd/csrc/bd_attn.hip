@@ -555,8 +555,9 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
     g = (int)(pair_a % a.Hkv);
     const int64_t nkeys = (int64_t)__builtin_amdgcn_readfirstlane(a.prefix_len[b]) + a.S;
     k_begin = (int64_t)split * im.chunk;
-    // a direct plan (one chunk) takes every key of the sequence
-    k_end = a.direct ? nkeys : min(k_begin + im.chunk, nkeys);
+    // the last chunk (and a direct plan's only one) runs to the sequence's end, so a length past
+    // the host's bound still has all its keys
+    k_end = a.direct || split == im.nsplit - 1 ? nkeys : min(k_begin + im.chunk, nkeys);
     item_out = (pair_a * im.nsplit + split) * a.row_tiles + rt;
     nsplit_out = im.nsplit;
   }

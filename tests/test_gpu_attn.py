@@ -226,13 +226,14 @@ def test_length_balanced_plan(case, num_splits, causal):
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
 
 
-@pytest.mark.parametrize("B,num_splits", [(5, 2), (5, 4), (80, 2), (80, 3), (5, 1), (80, 1)],
+@pytest.mark.parametrize("B,num_splits", [(5, 2), (5, 4), (80, 2), (80, 3), (5, 1), (80, 1), (1100, 2)],
                          ids=["wave-plan-2", "wave-plan-4", "group-plan-2", "group-plan-3", "one-chunk-5",
-                              "one-chunk-80"])
+                              "one-chunk-80", "uniform-plan-1100"])
 def test_lengths_above_the_host_bound(B, num_splits):
     """prefix_len above the descriptor's max_prefix_len (but within the cache): the device plan (per
-    wave up to 64 sequences, per work-group beyond) and the one-chunk plan still take every key of
-    every sequence, so the output matches the oracle over the true lengths."""
+    wave up to 64 sequences, per work-group up to 1024), the uniform plan beyond (its last chunk runs
+    to the sequence's end) and the one-chunk plan still take every key of every sequence, so the
+    output matches the oracle over the true lengths."""
     rng = np.random.default_rng(380 + B + num_splits)
     lens = rng.integers(0, 1500, size=B).astype(np.int32)
     lens[0] = 1500
