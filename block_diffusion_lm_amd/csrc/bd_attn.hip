@@ -16,10 +16,14 @@
 // the copies. Within a wave the 32-key blocks are software-pipelined: the QK product of the next
 // block is in flight while the current block's exponentials run.
 //
-// The host plans chunks for the whole batch; when only some sequences are still active (the
-// denoise loop retires sequences as their blocks complete) the kernels re-plan on the device:
-// the same grid is spread over the active sequences only, with proportionally shorter chunks,
-// so a partly retired batch still occupies every compute unit.
+// The host sizes the grid (B * nsplit chunk slots per KV head and row tile) from its bound on
+// the prefix lengths; the kernels then size the chunks on the device from the actual lengths and
+// active flags (balanced_plan, up to kMaxBalancedBatch sequences): a ragged batch gets chunks of
+// the size its total work calls for rather than its longest sequence's, and sequences the denoise
+// loop has retired give their slots to the active ones, so the grid keeps every compute unit
+// busy. Larger batches keep the host's uniform chunks, spread over the active sequences.
+// A chunk's partial result is (m, l) in float32 and its normalized output acc / l in bf16; the
+// merge kernel combines the chunks of every query row.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16). Scores are computed transposed,
 // S^T = K Q^T (A = 32 keys x 16 dims from LDS, B = Q^T held in registers), so that every lane
