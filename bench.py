@@ -331,19 +331,30 @@ def mamba_row(bd, dev):
     return res
 
 
+def code_sha256(source: str) -> str:
+    """SHA-256 of a source file's code: every line with its // comment and surrounding blanks
+    removed, blank lines dropped (comment edits leave it unchanged; any code change alters it)."""
+    import hashlib
+    import re
+    lines = []
+    with open(source) as f:
+        for line in f:
+            code = re.sub(r"//.*$", "", line).strip()
+            if code:
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def measured_traffic(kernel_source: str):
     """HBM traffic per launch of the attention split kernel from the committed counter summary
     (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a plain copy kernel), or None when the summary
-    is missing or was taken on a different kernel source."""
-    import hashlib
+    is missing or was taken on different kernel code."""
     path = os.path.join(ROOT, "profiles", "attn_split_long_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(kernel_source, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("code_sha256") != code_sha256(kernel_source):
         return None
     return rec.get("traffic_bytes_per_launch")
 

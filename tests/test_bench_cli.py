@@ -37,3 +37,17 @@ def test_attention_units_of_the_long_workload():
     assert fl / kv == 256
     fl1, kv1, _ = bench.attn_units(w, lens, np.array([True, False, False, False]))
     assert fl1 * 4 == fl and kv1 * 4 == kv
+
+
+def test_code_hash_ignores_comments_only(tmp_path):
+    """The counter summary is tied to the kernel's code: comment and blank-line edits keep the
+    hash, a code change alters it."""
+    import bench
+    a = tmp_path / "a.hip"
+    a.write_text("int f(int x) {  // doubles\n  return 2 * x;\n}\n")
+    b = tmp_path / "b.hip"
+    b.write_text("// header comment\n\nint f(int x) {  // twice x\n\n  return 2 * x;   \n}\n")
+    c = tmp_path / "c.hip"
+    c.write_text("int f(int x) {\n  return 3 * x;\n}\n")
+    assert bench.code_sha256(str(a)) == bench.code_sha256(str(b))
+    assert bench.code_sha256(str(a)) != bench.code_sha256(str(c))
