@@ -226,6 +226,28 @@ def test_length_balanced_plan(case, num_splits, causal):
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=LSE_ATOL)
 
 
+@pytest.mark.parametrize("B", [64, 65, 1024], ids=["wave-plan-edge-64", "group-plan-65", "group-plan-limit-1024"])
+def test_balanced_plan_at_its_batch_edges(B):
+    """The batch sizes where the device plan changes hands: 64 sequences (the last per-wave plan),
+    65 (the first per-work-group one) and 1024 (the largest balanced batch), ragged lengths and a
+    scattered active mask, every active row against the oracle."""
+    rng = np.random.default_rng(390 + B)
+    lens = rng.integers(0, 400, size=B).astype(np.int32)
+    w = I.small_workload(f"edge-{B}", B=B, Hq=4, Hkv=1, D=64, S=4, prefix_len=400, wid=391 + B)
+    inp = I.attn_inputs(w, lens=lens)
+    act = (rng.random(B) < 0.6).astype(np.uint8)
+    act[-1] = 1
+    plan = bd.attn_plan(bd.attn_desc(B, 4, 1, 64, 4, 400, 400, num_splits=3))
+    assert plan["num_splits"] > 1, plan
+    t = {k: dev_bf16(inp[k]) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
+    print(f"[attn] balanced-plan edge B={B} active={int(act.sum())} plan={plan}", flush=True)
+    out, _ = bd.attn_step(t["q"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], dev(inp["prefix_len"]),
+                          active=dev(act), num_splits=3, max_prefix_len=400)
+    torch.cuda.synchronize()
+    ref, _ = oracle_attn_all(inp, active=act)
+    assert_attn_close(host_f64(out[torch.from_numpy(act == 1).cuda()]), ref[act == 1], f"edge-{B}")
+
+
 @pytest.mark.parametrize("B,num_splits", [(5, 2), (5, 4), (80, 2), (80, 3), (5, 1), (80, 1), (1100, 2)],
                          ids=["wave-plan-2", "wave-plan-4", "group-plan-2", "group-plan-3", "one-chunk-5",
                               "one-chunk-80", "uniform-plan-1100"])
