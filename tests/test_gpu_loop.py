@@ -16,7 +16,7 @@ from tests.gpu_util import assert_attn_close, bf16_f64, dev, dev_bf16, host_f64,
 pytestmark = pytest.mark.gpu
 
 
-def run_loop(w, t0=0, mask0=None, tokens0=None, T=None, full_oracle=True):
+def run_loop(w, t0=0, mask0=None, tokens0=None, T=None, full_oracle=True, trace=None):
     T = w.T if T is None else T
     lens = I.prefix_lengths(w)
     cache = I.prefix_cache(w, lens)
@@ -38,9 +38,15 @@ def run_loop(w, t0=0, mask0=None, tokens0=None, T=None, full_oracle=True):
 
     kc, vc = dev_bf16(cache["k_cache"]), dev_bf16(cache["v_cache"])
     m_d, t_d = dev(mask0.copy()), dev(tokens0.copy())
-    res = bd.denoise_block(get_qkv, get_logits, kc, vc, dev(lens), m_d, t_d, T, w.Hq, w.gamma, w.S, w.V,
-                           logits_bf16=is_bf16, t0=t0, min_commit=bool(w.min_commit))
-    torch.cuda.synchronize()
+    if trace is not None:
+        trace.__enter__()
+    try:
+        res = bd.denoise_block(get_qkv, get_logits, kc, vc, dev(lens), m_d, t_d, T, w.Hq, w.gamma, w.S, w.V,
+                               logits_bf16=is_bf16, t0=t0, min_commit=bool(w.min_commit))
+        torch.cuda.synchronize()
+    finally:
+        if trace is not None:
+            trace.__exit__(None, None, None)
 
     f_cache = {k: bf16_f64(v) for k, v in cache.items()}
 
@@ -95,6 +101,25 @@ def test_small_loop_matches_oracle():
     w = I.small_workload("loop", B=3, Hq=8, Hkv=2, D=64, S=16, prefix_len=(50, 400), V=3000, logits_dtype="bf16",
                          sigma=3.0, gamma=0.9, mask_rule="frac", peaks=True, T=6, wid=250)
     run_loop(w)
+
+
+@pytest.mark.parametrize("B,S", [(4, 16), (2, 32), (1, 64), (5, 8), (6, 16), (3, 32)],
+                         ids=["4x16", "2x32", "1x64", "five-seqs-40-rows", "96-rows", "3x32-rows"])
+def test_loop_over_block_shapes(B, S):
+    """Loops over block lengths 8 to 64 and one to six sequences (masked rows found by a ballot up
+    to 64 rows, by the work-group scan above) match the oracle's loop bit for bit, through steps
+    where some or all sequences have finished: every step runs one reduction and one commit
+    launch, the commit of an empty step included (n_commit = 0, nothing left active)."""
+    w = I.small_workload(f"shape{B}x{S}", B=B, Hq=8, Hkv=2, D=64, S=S, prefix_len=(40, 300), V=2504,
+                         logits_dtype="bf16", sigma=3.0, gamma=0.9, mask_rule="frac", peaks=True, T=9, wid=260 + B * S)
+    tr = bd.Trace(capacity=256)
+    try:
+        res, ref = run_loop(w, trace=tr)
+        names = [n for n, _ in tr.records()]
+    finally:
+        tr.close()
+    assert names.count("vocab_reduce") == w.T and names.count("commit") == w.T
+    assert ref["steps_used"].max() < w.T, ref["steps_used"]
 
 
 def test_loop_resume_from_t0():
