@@ -284,8 +284,9 @@ MANY = [
 
 @pytest.mark.parametrize("case", MANY, ids=[c[0] for c in MANY])
 def test_many_sequences_with_a_ragged_active_mask(case):
-    """512 sequences, a seeded ragged active mask (first inactive, last active): the work-groups
-    find their sequence and the merge its partial rows through the work-group scan of the flags.
+    """512 sequences, a seeded ragged active mask (first inactive, last active): the split
+    work-groups find their sequence through the length-balanced plan over the active sequences
+    (derived per work-group), the merge its partial rows through the plan's stored prefix sums.
     Active rows match the oracle; inactive rows keep the canary fill."""
     name, Hq, Hkv, D, num_splits, waves = case
     B = 512
@@ -310,6 +311,37 @@ def test_many_sequences_with_a_ragged_active_mask(case):
     got = host_f64(out[torch.from_numpy(act == 1).cuda()])
     ref, _ = oracle_attn_all(inp, active=act)
     assert_attn_close(got, ref[act == 1], name)
+
+
+@pytest.mark.parametrize("Hq,waves", [(4, 4), (16, 8)], ids=["4w-64rows", "8w-256rows"])
+def test_uniform_plan_beyond_the_balanced_batch(Hq, waves):
+    """1100 sequences, above the largest balanced batch (1024), keep the uniform plan: under a
+    scattered active mask every split work-group finds its sequence, and the merge the partial rows
+    of its own, by counting the active flags in passes of one work-group's width (three passes of
+    512 flags, five of 256); active rows match the oracle, inactive rows keep the canary fill."""
+    B = 1100
+    rng = np.random.default_rng(395 + Hq)
+    lens = rng.integers(0, 400, size=B).astype(np.int32)
+    w = I.small_workload(f"uniform-{Hq}", B=B, Hq=Hq, Hkv=1, D=64, S=16, prefix_len=400, wid=396 + Hq)
+    inp = I.attn_inputs(w, lens=lens)
+    act = (rng.random(B) < 0.5).astype(np.uint8)
+    act[0], act[-1] = 0, 1
+    act[512:530] = 1   # a run of active flags across the first pass boundary of the wide kernel
+    plan = bd.attn_plan(bd.attn_desc(B, Hq, 1, 64, 16, 400, 400, num_splits=3))
+    assert plan["num_splits"] == 3 and plan["waves"] == waves, plan
+    print(f"[attn] uniform plan B={B} Hq={Hq} active={int(act.sum())} plan={plan}", flush=True)
+    t = {k: dev_bf16(inp[k]) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
+    big, out, gd = guarded(tuple(inp["q"].shape), torch.bfloat16)
+    b0 = big.clone()
+    bd.attn_step(t["q"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], dev(inp["prefix_len"]), active=dev(act),
+                 out=out, want_lse=False, num_splits=3, max_prefix_len=400)
+    torch.cuda.synchronize()
+    assert guards_intact(big, gd, out.numel(), b0)
+    keep = b0[gd:gd + out.numel()].view(out.shape)
+    ina = torch.from_numpy(act == 0).cuda()
+    assert torch.equal(out[ina].view(torch.int16), keep[ina].view(torch.int16))
+    ref, _ = oracle_attn_all(inp, active=act)
+    assert_attn_close(host_f64(out[torch.from_numpy(act == 1).cuda()]), ref[act == 1], f"uniform-{Hq}")
 
 
 @pytest.mark.parametrize("num_splits", [0, 1, 3])
