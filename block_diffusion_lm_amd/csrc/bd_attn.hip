@@ -82,6 +82,24 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Position of the k-th set bit of m (k < popcount(m)): a binary search on the halves' counts.
+__device__ __forceinline__ int select_bit(uint64_t m, int k) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const uint64_t lo = m & ((1ull << w) - 1);
+    const int c = __popcll(lo);
+    if (k >= c) {
+      k -= c;
+      m >>= w;
+      pos += w;
+    } else {
+      m = lo;
+    }
+  }
+  return pos;
+}
+
 // Device-side plan of one launch: which (sequence, KV head, chunk, row tile) a workgroup owns.
 // With every sequence active this is the host plan. With n_act < B active sequences the same
 // number of workgroups is spread over the active ones: splits per (sequence, KV head) grow to
@@ -1075,23 +1093,47 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int tile_ro
   const int rw = tid / (DG * CG);
   // the host keeps B * Hkv * rows below 2^31: 32-bit row arithmetic (no 64-bit division ahead of
   // the first load)
-  const uint32_t nrows = (uint32_t)a.B * a.Hkv * a.rows;
+  uint32_t nrows = (uint32_t)a.B * a.Hkv * a.rows;
+  uint32_t nitems = gridDim.x;
+  // With an active mask over at most 64 sequences the rows are numbered over the active sequences
+  // only and the first work-groups of the grid take them, so they spread over every XCD whichever
+  // sequences have retired (numbered over all sequences, a lone active sequence's rows would sit on
+  // the two XCDs that its quarter of the grid maps to).
+  const bool compact = a.active && a.B <= 64;
+  // (balanced plan over at most 64 sequences) the plan's prefix sums, one per lane, loaded together
+  // with the flags so that both cost one round trip: row k then takes its sequence's by shuffle
+  const bool lane_plan = a.balanced && a.B <= 64;
+  int pfx_l = 0, pfx_tot = 0;
+  if (lane_plan) {
+    const int ln = tid & 63;
+    pfx_l = a.plan_pfx[min(ln, a.B - 1)];
+    pfx_tot = a.plan_pfx[a.B];
+  }
+  uint64_t act_bits = 0;
+  if (compact) {
+    const int ln = tid & 63;
+    act_bits = __builtin_amdgcn_ballot_w64(ln < a.B && a.active[min(ln, a.B - 1)] != 0);
+    nrows = (uint32_t)__popcll(act_bits) * (uint32_t)a.Hkv * a.rows;
+    nitems = (nrows + RW * RPT - 1) / (RW * RPT);
+    if (blockIdx.x >= nitems) return;   // uniform
+  }
   int r[RPT], b[RPT], g[RPT];
   bool act[RPT];
   uint32_t plen[RPT];
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
     // consecutive rows on one XCD: their (m, l) pairs share cache sectors
-    const uint32_t rowg = (xcd_local_item(blockIdx.x, gridDim.x) * RPT + k) * RW + rw;
+    const uint32_t rowg = (xcd_local_item(blockIdx.x, nitems) * RPT + k) * RW + rw;
     const bool live = rowg < nrows;
     const uint32_t pair = live ? rowg / (uint32_t)a.rows : 0;
     r[k] = live ? (int)(rowg - pair * (uint32_t)a.rows) : 0;
-    b[k] = (int)(pair / (uint32_t)a.Hkv);
-    g[k] = (int)(pair - (uint32_t)b[k] * a.Hkv);
+    const int bn = (int)(pair / (uint32_t)a.Hkv);   // among the active sequences when compact
+    g[k] = (int)(pair - (uint32_t)bn * a.Hkv);
+    b[k] = compact && live ? select_bit(act_bits, bn) : bn;
     // (uniform plan) the sequence's length first: it is needed last (to drop the chunks past its
     // keys), and its load then overlaps the scan of the active flags and the partial loads
     plen[k] = live && !a.balanced ? a.prefix_len[b[k]] : 0;
-    act[k] = live && !(a.active && !a.active[b[k]]);
+    act[k] = live && (compact || !(a.active && !a.active[b[k]]));
   }
   // where row k's chunk partials are (p0[k] + c * pstride, c < nclamp[k]) under either plan; an
   // inactive row reads the workspace's first rows (in bounds, shared by all such rows) and drops
@@ -1108,9 +1150,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int tile_ro
     for (int k = 0; k < RPT; ++k) {
       p0[k] = 0;
       nclamp[k] = 0;
+      // (all lanes take part in the shuffles)
+      const int Pl = __shfl(pfx_l, b[k], 64);
+      const int Pnl = b[k] + 1 < a.B ? __shfl(pfx_l, b[k] + 1, 64) : pfx_tot;
       if (act[k]) {
-        const int P = a.plan_pfx[b[k]];
-        nclamp[k] = a.plan_pfx[b[k] + 1] - P;   // every chunk of the sequence holds keys
+        const int P = lane_plan ? Pl : a.plan_pfx[b[k]];
+        nclamp[k] = (lane_plan ? Pnl : a.plan_pfx[b[k] + 1]) - P;   // every chunk of the sequence holds keys
         const int rt = r[k] / tile_rows;
         p0[k] = (((int64_t)P * a.Hkv + g[k]) * a.row_tiles + rt) * tile_rows + (r[k] - rt * tile_rows);
       }
