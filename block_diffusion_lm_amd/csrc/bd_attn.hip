@@ -1016,9 +1016,50 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
       if (t + NSTAGE < ntiles) issue_tile(st, k_begin + (int64_t)(t + NSTAGE) * G::KT);
     }
   }
-  if (!wave_rows) return;
-
   // ---- epilogue: lane owns row lrow of each row block; dims db*32 + 8*(r/4) + 4*half + r%4
+  // The chunk partials go out through LDS: each wave stages its rows in the (now idle) tile ring and
+  // writes them back as whole 256-byte rows, 16 bytes a lane, instead of each lane's 8-byte pieces
+  // scattered over 32 rows (the write-back of the partials took ~5 us of a long step).
+  constexpr int PITCH = D * 2 + 16;   // staged row (bytes), padded so the rows' writes spread over the banks
+  static_assert(NW * RB * 32 * PITCH <= NSTAGE * G::STAGE, "the staged partials fit in the tile ring");
+  if (nsplit_out != 1) __syncthreads();   // uniform: every wave is done with the ring
+  if (!wave_rows) return;
+  if (nsplit_out != 1) {
+    char* stage = smem + wave * (RB * 32 * PITCH);
+    const int64_t prow0 = item_out * tile_rows + (row0 - rt * tile_rows);   // the wave's first partial row
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float l_tot = l_run[rb] + other_half(l_run[rb]);
+      // the normalized output acc / l in bf16 (zero for a chunk without a visible key) and (m, l)
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      const int rr = rb * 32 + lrow;
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = db * 32 + 8 * q4 + 4 * half;
+          bf16x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[rb][db][4 * q4 + i] * inv);
+          *reinterpret_cast<bf16x4*>(stage + rr * PITCH + d * 2) = v;
+        }
+      if (half == 0 && row0 + rr < a.rows)
+        *reinterpret_cast<float2*>(a.part_ml + (prow0 + rr) * 2) = make_float2(m_run[rb], l_tot);
+    }
+    // rows past a.rows in the last row tile are padding rows of the partial buffer (never read)
+    constexpr int CPR = D * 2 / 16;                 // 16-byte pieces of a row
+    constexpr int NIT = RB * 32 * CPR / 64;
+    char* ap = reinterpret_cast<char*>(a.part_o + prow0 * D);
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int e = j * 64 + lane;
+      const int row = e / CPR, c = e % CPR;
+      *reinterpret_cast<u32x4*>(ap + row * (D * 2) + c * 16) =
+          *reinterpret_cast<const u32x4*>(stage + row * PITCH + c * 16);
+    }
+    (void)NT;
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float l_tot = l_run[rb] + other_half(l_run[rb]);
@@ -1026,7 +1067,7 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
     if (r >= a.rows) continue;
     const int s = r / a.group;
     const int hq = g * a.group + (r - s * a.group);
-    if (nsplit_out == 1) {
+    {
       const float inv = 1.0f / l_tot;
       uint16_t* op = a.out + (((int64_t)b * a.S + s) * a.Hq + hq) * D;
 #pragma unroll
@@ -1040,26 +1081,6 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
           *reinterpret_cast<bf16x4*>(op + d) = v;
         }
       if (a.lse && half == 0) a.lse[((int64_t)b * a.Hq + hq) * a.S + s] = (m_run[rb] + log2f(l_tot)) * kLn2;
-    } else {
-      // partial of this chunk: (m, l) and the normalized output acc / l in bf16 (zero for a chunk
-      // without a visible key); merged by the merge kernel
-      const int64_t prow = item_out * tile_rows + (r - rt * tile_rows);
-      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-      uint16_t* ap = a.part_o + prow * D;
-#pragma unroll
-      for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d = db * 32 + 8 * q4 + 4 * half;
-          bf16x4 v;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[rb][db][4 * q4 + i] * inv);
-          *reinterpret_cast<bf16x4*>(ap + d) = v;
-        }
-      if (half == 0) {
-        a.part_ml[prow * 2] = m_run[rb];
-        a.part_ml[prow * 2 + 1] = l_tot;
-      }
     }
   }
   (void)NT;
