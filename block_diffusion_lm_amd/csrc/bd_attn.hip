@@ -22,8 +22,9 @@
 // the size its total work calls for rather than its longest sequence's, and sequences the denoise
 // loop has retired give their slots to the active ones, so the grid keeps every compute unit
 // busy. Larger batches keep the host's uniform chunks, spread over the active sequences.
-// A chunk's partial result is (m, l) in float32 and its normalized output acc / l in bf16; the
-// merge kernel combines the chunks of every query row.
+// A chunk's partial result is (m, l) in float32 and its normalized output acc / l in bf16, staged
+// through the idle tile ring so that it leaves as whole rows; the merge kernel combines the chunks
+// of every query row, its work-groups numbered over the active sequences' rows.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16). Scores are computed transposed,
 // S^T = K Q^T (A = 32 keys x 16 dims from LDS, B = Q^T held in registers), so that every lane
