@@ -209,6 +209,7 @@ bd_status run_attn(const bd_attn_desc* d, const bd::AttnPlan& plan, const void* 
   a.scale_log2 = tau * 1.4426950408889634f;
   a.direct = plan.direct ? 1 : 0;
   a.balanced = !plan.direct && d->batch <= bd::kMaxBalancedBatch ? 1 : 0;
+  a.stream_kv = (double)d->batch * d->n_kv_heads * (double)a.max_keys * d->head_dim * 4 > (double)bd::kStreamKvBytes;
   a.causal = d->causal;
   bd_status st = traced("attn_split", stream, [&](const bd::Launch& l) { return bd::launch_attn_split(plan, a, l); });
   if (st != BD_OK || plan.direct) return st;

@@ -477,14 +477,16 @@ __device__ __forceinline__ void dma16(const char* src, char* dst) {
 }
 
 // The same through a buffer resource: lane l's 16 bytes at base(rsrc) + soff + voff. The scalar
-// offset carries the tile position, so a tile costs no vector ALU work at all. The cached K/V
-// stream is read once per launch, so it goes with the non-temporal hint (cache policy bit 1 on
-// gfx950) and leaves the caches to the partials and the reused block rows (measured: the ragged
-// 8-KV-head batch 223 -> 204-209 us, a long step 0.5-3.5 us faster, the large batch unchanged).
+// offset carries the tile position, so a tile costs no vector ALU work at all. POLICY is the
+// cache policy of the load: kStreamPolicy (bit 1 on gfx950: non-temporal) for a cached K/V stream
+// too large to stay in the caches between launches, so that it leaves them to the partials and
+// the block rows; 0 (normal) for one small enough to be read again from the last-level cache by
+// the next launch (a decode step's 4 MB). The host picks (AttnArgs::stream_kv).
 constexpr int kStreamPolicy = 2;
+template <int POLICY = 0>
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, char* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0,
-                                           kStreamPolicy);
+                                           POLICY);
 }
 
 // Raw buffer resource over `bytes` bytes at `base` (dword 3: the gfx9 raw-buffer format word).
@@ -658,15 +660,28 @@ __global__ __launch_bounds__(NW * 64, NW * RB == 8 ? 1 : 2) void attn_split_kern
     char* dst = smem + stage * G::STAGE;
     if (kt0 + G::KT <= len && kt0 + G::KT <= k_end) {
       const uint32_t soff = (uint32_t)(kt0 * D * 2);
+      if (a.stream_kv) {   // uniform
 #pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        const int j = wave + NWD * i;
-        dma16_buf(rsrc_k, kl, soff + 1024 * j, dst + 1024 * j);
-      }
+        for (int i = 0; i < NK; ++i) {
+          const int j = wave + NWD * i;
+          dma16_buf<kStreamPolicy>(rsrc_k, kl, soff + 1024 * j, dst + 1024 * j);
+        }
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int j = wave + NWD * i;
-        dma16_buf(rsrc_v, vl, soff + 1024 * j, dst + G::KBYTES + 1024 * j);
+        for (int i = 0; i < NV; ++i) {
+          const int j = wave + NWD * i;
+          dma16_buf<kStreamPolicy>(rsrc_v, vl, soff + 1024 * j, dst + G::KBYTES + 1024 * j);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+          const int j = wave + NWD * i;
+          dma16_buf(rsrc_k, kl, soff + 1024 * j, dst + 1024 * j);
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const int j = wave + NWD * i;
+          dma16_buf(rsrc_v, vl, soff + 1024 * j, dst + G::KBYTES + 1024 * j);
+        }
       }
     } else {
       // per lane: cached rows through the cache resources, rows past the prefix end by a global

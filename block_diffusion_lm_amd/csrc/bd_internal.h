@@ -86,7 +86,12 @@ struct AttnArgs {
   int balanced;       // split launch over at most kMaxBalancedBatch sequences: chunks sized on the
                       // device from the actual lengths (see balanced_plan in bd_attn.hip)
   int causal;         // 1: block key j is visible to block position s only when j <= s
+  int stream_kv;      // 1: the cached K/V of one launch exceed kStreamKvBytes; loaded non-temporally
 };
+
+// K/V bytes of one launch (B Hkv (max_prefix_len + S) D, K and V, bf16) above which the split
+// kernel streams the cache past the caches: half the MI355X's 256 MB last-level cache.
+constexpr int64_t kStreamKvBytes = (int64_t)128 << 20;
 
 // Largest batch whose split launches plan their chunks from the actual prefix lengths on the device
 // (the work-groups keep one prefix-sum entry per sequence in LDS).
