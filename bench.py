@@ -331,6 +331,20 @@ def mamba_row(bd, dev):
     return res
 
 
+def per_step_kernel_us(recs, T: int, names=("attn_split", "attn_merge", "vocab_reduce", "commit")) -> dict:
+    """Median duration (us) of each loop kernel at each step t, over the traced calls: records are
+    (kernel, ms) in launch order and every call launches each kernel once per step; a kernel whose
+    launch count is not a multiple of T is left out."""
+    out = {}
+    for name in names:
+        ms = [m for n, m in recs if n == name]
+        if not ms or len(ms) % T:
+            continue
+        a = np.asarray(ms, np.float64).reshape(len(ms) // T, T)
+        out[name] = [round(float(v) * 1e3, 2) for v in np.median(a, axis=0)]
+    return out
+
+
 def code_sha256(source: str) -> str:
     """SHA-256 of a source file's code: every line with its // comment and surrounding blanks
     removed, blank lines dropped (comment edits leave it unchanged; any code change alters it)."""
@@ -529,7 +543,9 @@ def main():
             "reduce_avg_ms": round(float(np.mean(red_ms)), 5),
         },
         "loop": {"steps_used": steps_used.tolist(), "commits_per_step": commits.sum(axis=1).tolist(),
-                 "tokens_per_step": round(float(mask0.sum()) / max(1, int(steps_used.max())), 3)},
+                 "tokens_per_step": round(float(mask0.sum()) / max(1, int(steps_used.max())), 3),
+                 # where the loop's time goes, step by step (full, partly active and empty steps)
+                 "kernel_us_per_step": per_step_kernel_us(recs, T)},
         "roofline": {"kernel": "attn_split", "bound": "hbm", "achieved": round(achieved_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(os.path.join(ROOT, "block_diffusion_lm_amd", "csrc", "bd_attn.hip")),

@@ -51,3 +51,22 @@ def test_code_hash_ignores_comments_only(tmp_path):
     c.write_text("int f(int x) {\n  return 3 * x;\n}\n")
     assert bench.code_sha256(str(a)) == bench.code_sha256(str(b))
     assert bench.code_sha256(str(a)) != bench.code_sha256(str(c))
+
+
+def test_per_step_kernel_medians():
+    # two traced calls of a three-step loop: loop_init, then split / merge / reduce / commit per step
+    T, recs = 3, []
+    for call in range(2):
+        recs.append(("loop_init", 0.004))
+        for t in range(T):
+            recs += [("attn_split", 0.070 + 0.001 * t + 0.002 * call), ("attn_merge", 0.007),
+                     ("vocab_reduce", 0.009 - 0.001 * t), ("commit", 0.005)]
+    got = bench.per_step_kernel_us(recs, T)
+    assert got["attn_split"] == [71.0, 72.0, 73.0]     # median of the two calls at each step
+    assert got["vocab_reduce"] == [9.0, 8.0, 7.0]
+    assert got["commit"] == [5.0, 5.0, 5.0]
+    assert "loop_init" not in got
+    # a kernel launched a number of times that does not split into steps is left out
+    cut = bench.per_step_kernel_us(recs[:-2], T)    # the last reduction and commit missing
+    assert "vocab_reduce" not in cut and "commit" not in cut
+    assert cut["attn_merge"] == [7.0, 7.0, 7.0]
